@@ -1,0 +1,157 @@
+"""Seeded synthetic inputs shared by the oracle-side checks and the HIP path.
+
+This module holds no attention arithmetic.  It only draws Gaussian samples,
+rounds them to bfloat16 and names the workload shapes, so that both sides of a
+parity test consume the exact same bit patterns.
+
+Recipe (the pages name no dataset; every workload is synthetic):
+  * ``numpy.random.default_rng(seed)`` (PCG64);
+  * ``standard_normal(shape, dtype=float32)`` drawn in the order q, k, v;
+  * optionally multiplied by ``input_scale`` in float32 (the head-dim sweep
+    scales by 1/sqrt(d) before rounding);
+  * rounded to bfloat16 by round-to-nearest-even on the float32 bit pattern.
+
+Tensors are laid out ``[B][H][N][d]`` with d fastest.  Decode queries are
+``[B][Hq][d]`` (one query row per sequence).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+import math
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits_from_f32",
+    "f64_from_bf16_bits",
+    "f32_from_bf16_bits",
+    "gaussian_bf16",
+    "AttnConfig",
+    "CONFIGS",
+    "fwd_config",
+    "decode_config",
+    "make_fwd_inputs",
+    "make_decode_inputs",
+    "row_subset",
+]
+
+
+def bf16_bits_from_f32(x) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even).
+
+    Returns the 16-bit patterns as ``uint16``.  Inputs are finite Gaussian
+    samples, so NaN handling is not needed; infinities round to themselves.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = (u + 0x7FFF + lsb) >> 16
+    return r.astype(np.uint16)
+
+
+def f32_from_bf16_bits(bits) -> np.ndarray:
+    """Widen bfloat16 bit patterns to float32 (exact)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def f64_from_bf16_bits(bits) -> np.ndarray:
+    """Widen bfloat16 bit patterns to float64 (exact)."""
+    return f32_from_bf16_bits(bits).astype(np.float64)
+
+
+def gaussian_bf16(seed: int, shapes, input_scale: float = 1.0):
+    """Draw one bf16 tensor per shape from N(0,1), in order, from one generator."""
+    rng = np.random.default_rng(seed)
+    out = []
+    s32 = np.float32(input_scale)
+    for shp in shapes:
+        x = rng.standard_normal(shp, dtype=np.float32)
+        if input_scale != 1.0:
+            x = (x * s32).astype(np.float32)
+        out.append(bf16_bits_from_f32(x))
+    return out
+
+
+@dataclass(frozen=True)
+class AttnConfig:
+    """One synthetic workload.  ``kind`` is "fwd" or "decode"."""
+
+    name: str
+    kind: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    seed: int
+    input_scale: float = 1.0
+    splits: tuple = field(default_factory=tuple)
+
+    @property
+    def scale(self) -> float:
+        """Softmax scale: 1/sqrt(d) for every workload."""
+        return 1.0 / math.sqrt(self.d)
+
+    def flops(self) -> float:
+        """Algorithmic flop: 4*B*Hq*Nq*Nk*d, halved when causal (Nq == Nk)."""
+        f = 4.0 * self.B * self.Hq * self.Nq * self.Nk * self.d
+        return f / 2.0 if self.causal else f
+
+
+def fwd_config(name, B, H, N, d, causal, seed, input_scale=1.0, Hkv=None, Nk=None):
+    return AttnConfig(name, "fwd", B, H, Hkv or H, N, Nk or N, d, causal, seed,
+                      input_scale)
+
+
+def decode_config(name, B, Hq, Hkv, Nk, d, seed, splits=()):
+    return AttnConfig(name, "decode", B, Hq, Hkv, 1, Nk, d, False, seed, 1.0,
+                      tuple(splits))
+
+
+# The five workloads: a tiny non-causal case, a training-shape prefill (both
+# mask modes), a long-context causal prefill, a head-dim sweep and a GQA
+# split-KV decode over a 32k-token cache.
+CONFIGS = {
+    "tiny": fwd_config("tiny", 1, 2, 256, 64, False, seed=1),
+    "train_nc": fwd_config("train_nc", 8, 16, 2048, 128, False, seed=2),
+    "train_c": fwd_config("train_c", 8, 16, 2048, 128, True, seed=2),
+    "long": fwd_config("long", 1, 32, 16384, 128, True, seed=3),
+    "sweep_d32": fwd_config("sweep_d32", 2, 16, 4096, 32, True, seed=72,
+                            input_scale=1 / math.sqrt(32)),
+    "sweep_d64": fwd_config("sweep_d64", 2, 16, 4096, 64, True, seed=104,
+                            input_scale=1 / math.sqrt(64)),
+    "sweep_d128": fwd_config("sweep_d128", 2, 16, 4096, 128, True, seed=168,
+                             input_scale=1 / math.sqrt(128)),
+    "sweep_d256": fwd_config("sweep_d256", 2, 16, 4096, 256, True, seed=296,
+                             input_scale=1 / math.sqrt(256)),
+    "decode": decode_config("decode", 8, 32, 8, 32768, 128, seed=5,
+                            splits=(16, 32, 64)),
+}
+
+
+def make_fwd_inputs(cfg: AttnConfig):
+    """bf16 bits for q [B][Hq][Nq][d], k and v [B][Hkv][Nk][d]."""
+    return gaussian_bf16(
+        cfg.seed,
+        [(cfg.B, cfg.Hq, cfg.Nq, cfg.d), (cfg.B, cfg.Hkv, cfg.Nk, cfg.d),
+         (cfg.B, cfg.Hkv, cfg.Nk, cfg.d)],
+        cfg.input_scale)
+
+
+def make_decode_inputs(cfg: AttnConfig):
+    """bf16 bits for q [B][Hq][d], k_cache and v_cache [B][Hkv][Nk][d]."""
+    return gaussian_bf16(
+        cfg.seed,
+        [(cfg.B, cfg.Hq, cfg.d), (cfg.B, cfg.Hkv, cfg.Nk, cfg.d),
+         (cfg.B, cfg.Hkv, cfg.Nk, cfg.d)],
+        cfg.input_scale)
+
+
+def row_subset(N: int, count: int, head: int) -> np.ndarray:
+    """Seeded sorted subset of query rows checked for one head of a long case."""
+    rng = np.random.default_rng(1000 + head)
+    return np.sort(rng.choice(N, size=min(count, N), replace=False))

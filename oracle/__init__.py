@@ -1,0 +1,13 @@
+"""float64 CPU oracle: test infrastructure, never part of the product path.
+
+Only ``tests/``, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It shares no code with the HIP library.  See
+``oracle/attention.py`` for what each function computes and which passage of
+the pages it follows.
+"""
+
+from .attention import (allowed_keys, attention_head_ref, attention_ref,
+                        merge_partials, merge_ref, online_ref)
+
+__all__ = ["allowed_keys", "attention_head_ref", "attention_ref",
+           "merge_partials", "merge_ref", "online_ref"]
