@@ -1,0 +1,235 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one causal prefill forward over the long-context workload
+(B=1, H=32, N=16384, d=128) followed by one split-KV decode over the decode
+workload (B=8, Hq=32, Hkv=8, Nk=32768, d=128), both through the C ABI on the
+same stream, inputs already resident in HBM.  Prints one JSON line:
+
+  value     prefill TFLOP/s, flop = 4*B*H*N*N*d / 2 (causal), per forward
+            launch (HIP events on the launch stream, averaged over the steps)
+  decode    split-KV decode GB/s, bytes = K + V cache read once + q + O + LSE
+  roofline  the forward kernel against the dense bf16 MFMA peak (2.5 PFLOP/s);
+            decode carries its own roofline against 8 TB/s HBM
+  cpu_baseline  the float64 oracle on a bounded sample of the same workload,
+            timed on the host cores (rank 0, one GPU)
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import datagen  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+METRIC = "fused attn fwd TFLOP/s (% bf16 MFMA peak); split-KV decode HBM GB/s"
+
+
+def _dev(bits):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).to("cuda:0").contiguous()
+
+
+def _traffic(kernel, source_files):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when no summary exists or the kernel sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    for s in source_files:
+        with open(os.path.join(ROOT, s), "rb") as f:
+            h.update(f.read())
+    if rec.get("source_sha256") != h.hexdigest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline_fwd(cfg, qb, kb, vb, rows_per_head=512, heads=16):
+    """Oracle on `heads` heads x `rows_per_head` seeded rows of the prefill
+    workload; throughput counts the algorithmic (causal) flop of those rows."""
+    import oracle
+    q = datagen.f64_from_bf16_bits(qb[:, :heads])
+    k = datagen.f64_from_bf16_bits(kb[:, :heads])
+    v = datagen.f64_from_bf16_bits(vb[:, :heads])
+    rows = {h: datagen.row_subset(cfg.Nq, rows_per_head, h) for h in range(heads)}
+    t0 = time.perf_counter()
+    oracle.attention_ref(q, k, v, cfg.scale, cfg.causal, rows=rows)
+    dt = time.perf_counter() - t0
+    pairs = sum(int((r + 1).sum()) for r in rows.values()) if cfg.causal else \
+        heads * rows_per_head * cfg.Nk
+    flop = 4.0 * cfg.d * pairs * cfg.B
+    return dict(value=flop / dt / 1e12, unit="TFLOP/s", cores=_blas_threads(),
+                kind="oracle", seconds=round(dt, 3),
+                sample=f"float64 oracle, {heads} of {cfg.Hq} heads x {rows_per_head} seeded "
+                       f"query rows of the causal B={cfg.B} H={cfg.Hq} N={cfg.Nq} d={cfg.d} "
+                       f"prefill, scores materialised then masked")
+
+
+def cpu_baseline_decode(cfg, qb, kb, vb, batches=2):
+    import oracle
+    q = datagen.f64_from_bf16_bits(qb[:batches])
+    k = datagen.f64_from_bf16_bits(kb[:batches])
+    v = datagen.f64_from_bf16_bits(vb[:batches])
+    t0 = time.perf_counter()
+    oracle.attention_ref(q[:, :, None, :], k, v, cfg.scale, False)
+    dt = time.perf_counter() - t0
+    nbytes = 2 * batches * cfg.Hkv * cfg.Nk * cfg.d * 2
+    return dict(value=nbytes / dt / 1e9, unit="GB/s", cores=_blas_threads(), kind="oracle",
+                seconds=round(dt, 3),
+                sample=f"float64 oracle, {batches} of {cfg.B} sequences of the decode workload")
+
+
+def _blas_threads():
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        if os.environ.get(var):
+            try:
+                return int(os.environ[var])
+            except ValueError:
+                pass
+    return os.cpu_count()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--splits", type=int, default=0, help="decode splits (0 = heuristic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the kernels are single-GPU and this build has "
+              "no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_103_amd as fa
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    fcfg = datagen.CONFIGS["long"]
+    dcfg = datagen.CONFIGS["decode"]
+    fq, fk, fv = datagen.make_fwd_inputs(fcfg)
+    dq, dk, dv = datagen.make_decode_inputs(dcfg)
+    q, k, v = _dev(fq), _dev(fk), _dev(fv)
+    o = torch.empty_like(q)
+    lse = torch.empty((fcfg.B, fcfg.Hq, fcfg.Nq), dtype=torch.float32, device="cuda")
+    qd, kc, vc = _dev(dq), _dev(dk), _dev(dv)
+    od = torch.empty_like(qd)
+    lsed = torch.empty((dcfg.B, dcfg.Hq), dtype=torch.float32, device="cuda")
+    S = args.splits or fa.fa_decode_num_splits(dcfg.B, dcfg.Hq, dcfg.Hkv, dcfg.Nk, dcfg.d)
+    ws = torch.empty(fa.fa_decode_workspace_size(dcfg.B, dcfg.Hq, dcfg.d, S),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        rc = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       fcfg.B, fcfg.Hq, fcfg.Hkv, fcfg.Nq, fcfg.Nk, fcfg.d, fcfg.scale,
+                       int(fcfg.causal), sp)
+        if rc:
+            raise fa.FAError(rc, "fa_fwd")
+        if ev is not None:
+            ev[1].record(stream)
+        rc = fa.fa_decode_splitkv(qd.data_ptr(), kc.data_ptr(), vc.data_ptr(), od.data_ptr(),
+                                  lsed.data_ptr(), dcfg.B, dcfg.Hq, dcfg.Hkv, dcfg.Nk, dcfg.d,
+                                  dcfg.scale, S, ws.data_ptr(), ws.numel(), sp)
+        if rc:
+            raise fa.FAError(rc, "fa_decode_splitkv")
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    f_ms = float(np.mean(fwd_ms))
+    d_ms = float(np.mean(dec_ms))
+
+    flop = fcfg.flops()
+    tflops = flop / (f_ms * 1e-3) / 1e12
+    dec_bytes = (2 * dcfg.B * dcfg.Hkv * dcfg.Nk * dcfg.d * 2 + 2 * dcfg.B * dcfg.Hq * dcfg.d * 2
+                 + 4 * dcfg.B * dcfg.Hq)
+    gbs = dec_bytes / (d_ms * 1e-3) / 1e9
+    fwd_bytes = 4 * fcfg.B * fcfg.Hq * fcfg.Nq * fcfg.d * 2 + 4 * fcfg.B * fcfg.Hq * fcfg.Nq
+    srcs = ["exact_attention_103_amd/csrc/fa_fwd.hip", "exact_attention_103_amd/csrc/fa_internal.h"]
+    dsrcs = ["exact_attention_103_amd/csrc/fa_decode.hip", "exact_attention_103_amd/csrc/fa_internal.h"]
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) float32 rounded to bf16",
+        "config": {
+            "workload": "causal prefill B=1 H=32 N=16384 d=128 + split-KV decode B=8 Hq=32 "
+                        "Hkv=8 Nk=32768 d=128",
+            "fwd": {"B": fcfg.B, "H": fcfg.Hq, "N": fcfg.Nq, "d": fcfg.d, "causal": True,
+                    "scale": fcfg.scale, "kernel": fa.fa_fwd_kernel_name(fcfg.d, 1),
+                    "flop": flop, "ms": round(f_ms, 5), "ms_min": round(min(fwd_ms), 5)},
+            "decode": {"B": dcfg.B, "Hq": dcfg.Hq, "Hkv": dcfg.Hkv, "Nk": dcfg.Nk, "d": dcfg.d,
+                       "splits": S,
+                       "kernels": [fa.fa_decode_kernel_name(dcfg.d, dcfg.Hq // dcfg.Hkv, 0),
+                                   fa.fa_decode_kernel_name(dcfg.d, dcfg.Hq // dcfg.Hkv, 1)],
+                       "bytes": dec_bytes, "ms": round(d_ms, 5), "ms_min": round(min(dec_ms), 5)},
+            "parallelism": "1 GPU",
+        },
+        "fwd_pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": _traffic("fa_fwd_d128_causal", srcs),
+            "kernel": fa.fa_fwd_kernel_name(fcfg.d, 1),
+            "algorithmic_bytes": fwd_bytes,
+        },
+        "decode": {
+            "value": round(gbs, 1), "unit": "GB/s", "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": _traffic("fa_decode_split_d128_g4", dsrcs)},
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_fwd(fcfg, fq, fk, fv)
+        out["decode"]["cpu_baseline"] = cpu_baseline_decode(dcfg, dq, dk, dv)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

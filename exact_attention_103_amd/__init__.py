@@ -1,0 +1,197 @@
+"""Exact fused attention forward and split-KV decode for MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of ``libfa.so`` (declared in
+``include/fa.h``).  The functions named like the C entry points take raw
+device pointers and sizes; ``fwd`` and ``decode`` accept torch tensors,
+allocate outputs (and the decode workspace) with torch and pass torch's
+current HIP stream.  Every step of the computation runs in the HIP kernels:
+if the library is missing this module raises instead of computing anything.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "FAError", "lib", "fa_fwd", "fa_decode_splitkv", "fa_decode_workspace_size",
+    "fa_decode_num_splits", "fa_decode_max_splits", "fa_strerror",
+    "fa_last_hip_error", "fa_fwd_kernel_name", "fa_decode_kernel_name",
+    "fwd", "decode", "EXPORTED_SYMBOLS", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_OK = 0
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+_cs = ctypes.c_char_p
+
+# name -> (restype, argtypes); mirrors include/fa.h
+_SIGNATURES = {
+    "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "fa_decode_splitkv": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
+                               _vp, _sz, _vp]),
+    "fa_decode_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "fa_decode_num_splits": (_i, [_i, _i, _i, _i, _i]),
+    "fa_decode_max_splits": (_i, [_i]),
+    "fa_strerror": (_cs, [_i]),
+    "fa_last_hip_error": (_cs, []),
+    "fa_fwd_kernel_name": (_cs, [_i, _i]),
+    "fa_decode_kernel_name": (_cs, [_i, _i, _i]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGNATURES)
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    """A negative status returned by libfa.so."""
+
+    def __init__(self, status: int, where: str):
+        text = lib().fa_strerror(status).decode()
+        if status == -7:
+            text += " (" + lib().fa_last_hip_error().decode() + ")"
+        super().__init__(f"{where}: {text} [status {status}]")
+        self.status = status
+
+
+def lib():
+    """Load libfa.so (built in-tree).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m exact_attention_103_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+# --- Entry points with the C names: raw pointers (ints) and sizes. ---------
+
+def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, stream=None):
+    return lib().fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, int(causal),
+                        stream)
+
+
+def fa_decode_splitkv(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nk, d, scale,
+                      num_splits, workspace, workspace_bytes, stream=None):
+    return lib().fa_decode_splitkv(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nk, d,
+                                   scale, num_splits, workspace, workspace_bytes,
+                                   stream)
+
+
+def fa_decode_workspace_size(B, Hq, d, num_splits):
+    return lib().fa_decode_workspace_size(B, Hq, d, num_splits)
+
+
+def fa_decode_num_splits(B, Hq, Hkv, Nk, d):
+    return lib().fa_decode_num_splits(B, Hq, Hkv, Nk, d)
+
+
+def fa_decode_max_splits(Nk):
+    return lib().fa_decode_max_splits(Nk)
+
+
+def fa_strerror(status):
+    return lib().fa_strerror(status).decode()
+
+
+def fa_last_hip_error():
+    return lib().fa_last_hip_error().decode()
+
+
+def fa_fwd_kernel_name(d, causal):
+    r = lib().fa_fwd_kernel_name(d, int(causal))
+    return r.decode() if r else None
+
+
+def fa_decode_kernel_name(d, hq_per_kv, stage):
+    r = lib().fa_decode_kernel_name(d, hq_per_kv, stage)
+    return r.decode() if r else None
+
+
+# --- torch-facing helpers (marshalling only). ------------------------------
+
+def _check_bf16(name, t, ndim):
+    import torch
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_ptr():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """O, LSE = attention(q, k, v); q [B][Hq][Nq][d], k/v [B][Hkv][Nk][d] bf16."""
+    import torch
+    _check_bf16("q", q, 4)
+    _check_bf16("k", k, 4)
+    _check_bf16("v", v, 4)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B][Hkv][Nk][d] with q's B and d")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), _stream_ptr())
+    if rc != FA_OK:
+        raise FAError(rc, "fa_fwd")
+    return out, lse
+
+
+def decode(q, k_cache, v_cache, scale=None, num_splits=0, out=None, lse=None,
+           workspace=None):
+    """Split-KV decode: q [B][Hq][d], caches [B][Hkv][Nk][d] bf16 -> O, LSE."""
+    import torch
+    _check_bf16("q", q, 3)
+    _check_bf16("k_cache", k_cache, 4)
+    _check_bf16("v_cache", v_cache, 4)
+    B, Hq, d = q.shape
+    Hkv, Nk = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, Nk, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("caches must be [B][Hkv][Nk][d] with q's B and d")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    S = num_splits
+    if S == 0:
+        S = fa_decode_num_splits(B, Hq, Hkv, Nk, d)
+        if S < 0:
+            raise FAError(S, "fa_decode_num_splits")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = fa_decode_workspace_size(B, Hq, d, S)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    rc = fa_decode_splitkv(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                           out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nk, d,
+                           float(scale), S, workspace.data_ptr(), workspace.numel(),
+                           _stream_ptr())
+    if rc != FA_OK:
+        raise FAError(rc, "fa_decode_splitkv")
+    return out, lse

@@ -1,0 +1,212 @@
+// C-ABI layer of libfa.so: argument validation, dispatch and error text.
+// Every check runs on the host before the first HIP call, so an invalid call
+// enqueues nothing and writes nothing (the declarations in include/fa.h give
+// the full contract).
+
+#include "fa.h"
+#include "fa_internal.h"
+
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+namespace {
+
+thread_local char g_hip_error[256] = "";
+
+int hip_fail(hipError_t e) {
+  snprintf(g_hip_error, sizeof(g_hip_error), "%s: %s", hipGetErrorName(e),
+           hipGetErrorString(e));
+  return FA_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_d(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
+
+// Product of positive factors, or -1 when it exceeds 2^62.
+int64_t checked_product(std::initializer_list<int64_t> xs) {
+  const int64_t lim = int64_t(1) << 62;
+  int64_t r = 1;
+  for (int64_t x : xs) {
+    if (x <= 0) return -1;
+    if (r > lim / x) return -1;
+    r *= x;
+  }
+  return r;
+}
+
+struct Span {
+  uintptr_t lo, hi;
+};
+
+Span span(const void* p, int64_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return {a, a + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
+
+int max_splits(int Nk) { return Nk <= 0 ? 0 : (Nk + fa::kDecodeChunkAlign - 1) / fa::kDecodeChunkAlign; }
+
+int split_chunk(int Nk, int S) {
+  const int c = (Nk + S - 1) / S;
+  return (c + fa::kDecodeChunkAlign - 1) / fa::kDecodeChunkAlign * fa::kDecodeChunkAlign;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+           int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (causal && Nq > Nk) return FA_ERR_SHAPE;
+  if (!supported_d(d)) return FA_ERR_HEAD_DIM;
+  if (!scale_ok(scale)) return FA_ERR_SCALE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+
+  const int64_t q_bytes = checked_product({B, Hq, Nq, d, 2});
+  const int64_t kv_bytes = checked_product({B, Hkv, Nk, d, 2});
+  const int64_t lse_bytes = checked_product({B, Hq, Nq, 4});
+  const fa::FwdTile t = fa::fwd_tile(d);
+  const int64_t grid = checked_product({(Nq + t.bm - 1) / t.bm, B, Hq});
+  if (q_bytes < 0 || kv_bytes < 0 || lse_bytes < 0 || grid < 0 || grid > INT32_MAX)
+    return FA_ERR_TOO_LARGE;
+
+  const Span sq = span(q, q_bytes), sk = span(k, kv_bytes), sv = span(v, kv_bytes);
+  const Span so = span(o, q_bytes), sl = span(lse, lse_bytes);
+  if (overlaps(so, sq) || overlaps(so, sk) || overlaps(so, sv) || overlaps(sl, sq) ||
+      overlaps(sl, sk) || overlaps(sl, sv) || overlaps(so, sl))
+    return FA_ERR_ALIAS;
+
+  fa::FwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.group = Hq / Hkv;
+  p.c = scale * fa::kLog2e;
+  const hipError_t e = fa::launch_fwd(p, d, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : hip_fail(e);
+}
+
+int fa_decode_max_splits(int Nk) { return max_splits(Nk); }
+
+size_t fa_decode_workspace_size(int B, int Hq, int d, int num_splits) {
+  if (!supported_d(d)) return 0;
+  const int64_t n = checked_product({B, Hq, num_splits, d + 1, 4});
+  return n < 0 ? 0 : static_cast<size_t>(n);
+}
+
+int fa_decode_num_splits(int B, int Hq, int Hkv, int Nk, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nk <= 0 || Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (!supported_d(d)) return FA_ERR_HEAD_DIM;
+  const int group = Hq / Hkv;
+  const int64_t per_split = checked_product({B, Hkv, group / fa::decode_group_tile(group)});
+  if (per_split < 0) return FA_ERR_TOO_LARGE;
+  // About 2048 workgroups (8 per CU on 256 CUs), chunks of >= 256 keys.
+  int64_t s = (2048 + per_split - 1) / per_split;
+  const int64_t by_len = Nk / 256 > 0 ? Nk / 256 : 1;
+  if (s > by_len) s = by_len;
+  if (s > max_splits(Nk)) s = max_splits(Nk);
+  if (s < 1) s = 1;
+  return static_cast<int>(s);
+}
+
+int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache, void* o,
+                      float* lse, int B, int Hq, int Hkv, int Nk, int d, float scale,
+                      int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !o || !lse) return FA_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nk <= 0) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (!supported_d(d)) return FA_ERR_HEAD_DIM;
+  if (!scale_ok(scale)) return FA_ERR_SCALE;
+  if (num_splits < 0 || num_splits > max_splits(Nk)) return FA_ERR_SPLITS;
+  const int S = num_splits == 0 ? fa_decode_num_splits(B, Hq, Hkv, Nk, d) : num_splits;
+  if (S < 0) return S;
+  const size_t need = fa_decode_workspace_size(B, Hq, d, S);
+  if (need == 0) return FA_ERR_TOO_LARGE;
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+      !aligned16(lse) || !aligned16(workspace))
+    return FA_ERR_ALIGN;
+
+  const int group = Hq / Hkv;
+  const int64_t q_bytes = checked_product({B, Hq, d, 2});
+  const int64_t kv_bytes = checked_product({B, Hkv, Nk, d, 2});
+  const int64_t lse_bytes = checked_product({B, Hq, 4});
+  const int64_t grid = checked_product({B, Hkv, S, group / fa::decode_group_tile(group)});
+  if (q_bytes < 0 || kv_bytes < 0 || lse_bytes < 0 || grid < 0 || grid > INT32_MAX)
+    return FA_ERR_TOO_LARGE;
+
+  const Span sq = span(q, q_bytes), sk = span(k_cache, kv_bytes), sv = span(v_cache, kv_bytes);
+  const Span so = span(o, q_bytes), sl = span(lse, lse_bytes);
+  const Span sw = span(workspace, static_cast<int64_t>(need));
+  const Span ins[3] = {sq, sk, sv};
+  for (const Span& in : ins)
+    if (overlaps(so, in) || overlaps(sl, in) || overlaps(sw, in)) return FA_ERR_ALIAS;
+  if (overlaps(so, sl) || overlaps(so, sw) || overlaps(sl, sw)) return FA_ERR_ALIAS;
+
+  fa::DecodeParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k_cache);
+  p.v = static_cast<const uint16_t*>(v_cache);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.o_part = static_cast<float*>(workspace);
+  p.lse_part = p.o_part + static_cast<size_t>(B) * Hq * S * d;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nk = Nk;
+  p.group = group;
+  p.splits = S;
+  p.chunk = split_chunk(Nk, S);
+  p.c = scale * fa::kLog2e;
+  const hipError_t e = fa::launch_decode(p, d, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : hip_fail(e);
+}
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid shape (sizes must be > 0, Hq a multiple of Hkv, causal needs Nq <= Nk)";
+    case FA_ERR_HEAD_DIM: return "unsupported head dimension (32, 64, 128 or 256)";
+    case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case FA_ERR_WORKSPACE: return "decode workspace is NULL or too small";
+    case FA_ERR_SPLITS: return "num_splits out of range";
+    case FA_ERR_HIP: return "HIP launch failed";
+    case FA_ERR_SCALE: return "scale must be finite and > 0";
+    case FA_ERR_ALIAS: return "an output overlaps an input or another output";
+    case FA_ERR_TOO_LARGE: return "sizes exceed the supported range";
+    default: return "unknown status";
+  }
+}
+
+const char* fa_last_hip_error(void) { return g_hip_error; }
+
+const char* fa_fwd_kernel_name(int d, int causal) {
+  if (causal != 0 && causal != 1) return nullptr;
+  return fa::fwd_kernel_name(d, causal != 0);
+}
+
+const char* fa_decode_kernel_name(int d, int hq_per_kv, int stage) {
+  return fa::decode_kernel_name(d, hq_per_kv, stage);
+}
+
+}  // extern "C"

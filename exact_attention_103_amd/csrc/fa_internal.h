@@ -1,0 +1,66 @@
+// Internal declarations shared by the kernels and the C-ABI layer of libfa.so.
+// Everything here is device-side plumbing for gfx950 (CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Arguments of one forward launch.  Tensors are [B][H][N][d] bf16 (raw
+// 16-bit words), LSE fp32.  c = scale * log2(e): scores are kept in base-2
+// units so that the exponential is a single v_exp_f32.
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int B, Hq, Hkv, Nq, Nk;
+  int group;     // Hq / Hkv
+  float c;       // scale * log2(e)
+};
+
+// Arguments of one split-KV decode (split kernel + merge kernel).
+struct DecodeParams {
+  const uint16_t* q;      // [B][Hq][d]
+  const uint16_t* k;      // [B][Hkv][Nk][d]
+  const uint16_t* v;
+  uint16_t* o;            // [B][Hq][d]
+  float* lse;             // [B][Hq]
+  float* o_part;          // [B][Hq][S][d]   chunk-normalised partial outputs
+  float* lse_part;        // [B][Hq][S]      chunk LSE (natural log), -inf if empty
+  int B, Hq, Hkv, Nk;
+  int group;              // Hq / Hkv
+  int splits;             // S
+  int chunk;              // keys per split (multiple of 64)
+  float c;                // scale * log2(e)
+};
+
+// Host-side launchers (defined next to their kernels).  They assume the
+// arguments were validated and return the hipError_t of the launch.
+hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t s);
+const char* fwd_kernel_name(int d, bool causal);
+const char* decode_kernel_name(int d, int group, int stage);
+
+// Tile shape of the forward kernel for head dimension d (BM = 32 * waves).
+struct FwdTile { int bm, bn, waves; };
+FwdTile fwd_tile(int d);
+
+// Query heads handled by one decode split workgroup: the largest of 8, 4, 2,
+// 1 that divides the number of query heads per KV head.
+int decode_group_tile(int group);
+
+// Keys per decode split are rounded up to this multiple.
+constexpr int kDecodeChunkAlign = 64;
+
+}  // namespace fa

@@ -1,0 +1,140 @@
+/*
+ * fa.h -- C ABI of libfa.so: exact fused attention forward and split-KV
+ * decode for AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (short names):
+ *   [Evolution]  "FlashAttention evolution" (sandeep007734.github.io,
+ *                posts/flashattention-evolution)
+ *   [Kruglikov]  "Flash Attention" (vladislavkruglikov.com,
+ *                articles/flash-attention)
+ *
+ * Conventions shared by every entry point
+ *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
+ *     allocates no memory and keeps no state between calls (apart from the
+ *     thread-local text of the last HIP error).  Calls from several host
+ *     threads are safe.
+ *   - Layout: [B][H][N][d] contiguous, d fastest, bf16 (IEEE bfloat16 bit
+ *     patterns in 16-bit words).  LSE is fp32.  Every tensor pointer must be
+ *     16-byte aligned.
+ *   - Calls only enqueue work on `stream` (a hipStream_t; NULL means the
+ *     default stream) and return; nothing is synchronised.  A fault inside a
+ *     kernel surfaces at the caller's next synchronisation.
+ *   - Every argument check runs before any HIP call.  On a negative return
+ *     nothing was enqueued and no output byte was written.
+ *   - Results are deterministic: no atomics, fixed reduction order.
+ *   - Non-finite inputs are not checked; the result is then undefined.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,       /* a required pointer is NULL                      */
+  FA_ERR_SHAPE = -2,      /* B, H or N <= 0, Hq % Hkv != 0, causal && Nq > Nk */
+  FA_ERR_HEAD_DIM = -3,   /* d not in {32, 64, 128, 256}                     */
+  FA_ERR_ALIGN = -4,      /* a tensor pointer is not 16-byte aligned         */
+  FA_ERR_WORKSPACE = -5,  /* decode workspace NULL or smaller than required  */
+  FA_ERR_SPLITS = -6,     /* num_splits outside 0 .. fa_decode_max_splits()  */
+  FA_ERR_HIP = -7,        /* a HIP launch failed; see fa_last_hip_error()    */
+  FA_ERR_SCALE = -8,      /* scale not finite or not > 0                     */
+  FA_ERR_ALIAS = -9,      /* an output overlaps an input or another output   */
+  FA_ERR_TOO_LARGE = -10  /* sizes exceed the 2^31 grid / 2^62 byte limits   */
+};
+
+/*
+ * fa_fwd -- exact attention forward with per-row log-sum-exp.
+ *
+ * Computes, for every batch b, query head h, query row i:
+ *   O[b,h,i,:] = sum_j P[i,j] V[b,g,j,:],   P = softmax_j(scale * Q K^T)
+ *   LSE[b,h,i] = ln sum_{j allowed} exp(scale * q_i . k_j)
+ * with g = h / (Hq / Hkv) (grouped-query heads share a KV head).  This is the
+ * function of [Evolution] §1 (the equation under "The Invariant and the
+ * Moving Bottleneck") with the scale of [Kruglikov]'s scaled dot-product
+ * attention; as [Kruglikov] "The IO problem" describes, only O and one
+ * number per row (here the natural-log LSE) are written, the score and
+ * probability tiles never leave the chip.
+ *
+ * causal = 1 keeps key j for row i iff j <= i + (Nk - Nq) (bottom-right
+ * aligned; j <= i when Nq == Nk).  causal with Nq > Nk is rejected so that no
+ * row is empty.
+ *
+ *   q      bf16 [B][Hq][Nq][d]
+ *   k, v   bf16 [B][Hkv][Nk][d]
+ *   o      bf16 [B][Hq][Nq][d]   output, rounded to nearest even
+ *   lse    fp32 [B][Hq][Nq]      output, natural log
+ *   scale  finite, > 0 (1/sqrt(d) for standard attention)
+ *   causal 0 or 1
+ *   stream hipStream_t or NULL
+ * Returns FA_OK or a negative fa_status.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+           int causal, void* stream);
+
+/*
+ * Split-KV decode ([Evolution] §6, Flash-Decoding): one query row per
+ * sequence against a long KV cache.  The keys are cut into num_splits
+ * contiguous chunks; one kernel computes, per (b, KV head, chunk), the
+ * chunk-normalised partial output and chunk LSE for all query heads of that
+ * KV head (each K/V byte is read once per KV head); a second kernel merges
+ * the chunks with the log-sum-exp identity:
+ *   M = max_s LSE_s,  w_s = exp(LSE_s - M),
+ *   O = sum_s w_s O_s / sum_s w_s,  LSE = M + ln sum_s w_s.
+ * Chunks are ceil(Nk / num_splits) keys rounded up to a multiple of 64; a
+ * chunk that falls past Nk is empty and gets weight 0.
+ *
+ *   q         bf16 [B][Hq][d]
+ *   k_cache   bf16 [B][Hkv][Nk][d]
+ *   v_cache   bf16 [B][Hkv][Nk][d]
+ *   o         bf16 [B][Hq][d]       output
+ *   lse       fp32 [B][Hq]          output, natural log
+ *   num_splits 0 = fa_decode_num_splits(B, Hq, Hkv, Nk, d), else
+ *             1 .. fa_decode_max_splits(Nk)
+ *   workspace device scratch of at least
+ *             fa_decode_workspace_size(B, Hq, d, splits) bytes (splits after
+ *             the 0 -> heuristic substitution), 16-byte aligned, owned by the
+ *             caller; it must not overlap any tensor argument.  Its contents
+ *             on return are unspecified.
+ */
+int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                      void* o, float* lse, int B, int Hq, int Hkv, int Nk,
+                      int d, float scale, int num_splits, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Bytes of decode workspace: fp32 partial outputs [B][Hq][S][d] followed by
+ * fp32 partial LSEs [B][Hq][S], i.e. 4*B*Hq*S*(d+1).  0 on invalid sizes. */
+size_t fa_decode_workspace_size(int B, int Hq, int d, int num_splits);
+
+/* Split count used when num_splits == 0: enough (b, KV head, chunk) work
+ * groups to fill the GPU several times over, chunks of at least 256 keys.
+ * Returns a value in 1 .. fa_decode_max_splits(Nk), or a negative fa_status
+ * for invalid sizes. */
+int fa_decode_num_splits(int B, int Hq, int Hkv, int Nk, int d);
+
+/* Largest accepted num_splits for a cache of Nk keys: ceil(Nk / 64). */
+int fa_decode_max_splits(int Nk);
+
+/* Static text for a status code. */
+const char* fa_strerror(int status);
+
+/* Text of the last HIP error seen by this host thread ("" if none). */
+const char* fa_last_hip_error(void);
+
+/* Kernel symbol names, as a profiler reports them, so a benchmark can
+ * confirm which kernel ran.  NULL for an unsupported head dimension.
+ * fa_decode_kernel_name: stage 0 = split kernel (depends on the number of
+ * query heads per KV head), stage 1 = merge kernel. */
+const char* fa_fwd_kernel_name(int d, int causal);
+const char* fa_decode_kernel_name(int d, int hq_per_kv, int stage);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */
