@@ -23,7 +23,7 @@ SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_decode.hip"]
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wno-unused-command-line-argument",
+    "-Wno-unused-command-line-argument", "-fno-honor-nans",
 ]
 
 

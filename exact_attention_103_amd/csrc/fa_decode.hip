@@ -251,28 +251,57 @@ __device__ __forceinline__ void decode_split_body(const DecodeParams& p, float* 
   }
 }
 
-// Merge: one workgroup per (b, query head).
+// Merge: one workgroup of kMergeThreads per (b, query head).  The split
+// LSEs are read in parallel and reduced through LDS; then thread t sums the
+// splits s = t / D, t / D + SP, ... for output column t % D with independent
+// loads, and the SP partial sums per column are added in a fixed order.
+constexpr int kMergeThreads = 256;
+
 template <int D>
 __device__ __forceinline__ void decode_merge_body(const DecodeParams& p) {
+  constexpr int SP = kMergeThreads / D;       // split phases per column
+  __shared__ float red[kMergeThreads];
+  __shared__ float part[kMergeThreads];
+  const int tid = threadIdx.x;
   const int bh = blockIdx.x;
   const int S = p.splits;
   const float* lp = p.lse_part + (size_t)bh * S;
   const float* op = p.o_part + (size_t)bh * S * D;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = max_raw(M, lp[s]);
-  float W = 0.f;
-  for (int s = 0; s < S; ++s) W += lp[s] == -INFINITY ? 0.f : expf(lp[s] - M);
-  const float inv = 1.0f / W;
-  for (int dd = threadIdx.x; dd < D; dd += blockDim.x) {
-    float O = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float w = lp[s] == -INFINITY ? 0.f : expf(lp[s] - M);
-      O += w * op[(size_t)s * D + dd];
-    }
-    bf16x2 v = {(__bf16)(O * inv), (__bf16)0.f};
-    p.o[(size_t)bh * D + dd] = __builtin_bit_cast(unsigned, v) & 0xFFFFu;
+
+  float mx = -INFINITY;
+  for (int s = tid; s < S; s += kMergeThreads) mx = max_raw(mx, lp[s]);
+  red[tid] = mx;
+  __syncthreads();
+  for (int w = kMergeThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = max_raw(red[tid], red[tid + w]);
+    __syncthreads();
   }
-  if (threadIdx.x == 0) p.lse[bh] = M + logf(W);
+  const float M = red[0];   // finite: chunk 0 always holds at least one key
+  __syncthreads();
+
+  const int dd = tid % D, ph = tid / D;
+  float O = 0.f, W = 0.f;
+#pragma unroll 8
+  for (int s = ph; s < S; s += SP) {
+    const float ls = lp[s];
+    const float w = ls == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ls - M) * kLog2e);
+    W += w;
+    O += w * op[(size_t)s * D + dd];
+  }
+  part[tid] = O;
+  red[tid] = W;
+  __syncthreads();
+  if (ph == 0) {
+    float Ot = 0.f, Wt = 0.f;
+#pragma unroll
+    for (int q = 0; q < SP; ++q) {
+      Ot += part[q * D + dd];
+      Wt += red[q * D + dd];
+    }
+    bf16x2 v = {(__bf16)(Ot / Wt), (__bf16)0.f};
+    p.o[(size_t)bh * D + dd] = __builtin_bit_cast(unsigned, v) & 0xFFFFu;
+    if (dd == 0) p.lse[bh] = M + logf(Wt);
+  }
 }
 
 }  // namespace
@@ -287,7 +316,7 @@ __device__ __forceinline__ void decode_merge_body(const DecodeParams& p) {
   }
 
 #define FA_DEC_MERGE(D)                                                               \
-  extern "C" __global__ void __launch_bounds__(128) fa_decode_merge_d##D(             \
+  extern "C" __global__ void __launch_bounds__(fa::kMergeThreads) fa_decode_merge_d##D( \
       fa::DecodeParams p) {                                                           \
     fa::decode_merge_body<D>(p);                                                      \
   }
@@ -377,7 +406,7 @@ hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t s) {
   const unsigned n1 = (unsigned)(p.B * p.Hkv * p.splits * (p.group / gt));
   hipError_t e = hipLaunchKernel(f1, dim3(n1), dim3(kDecThreads), args, 0, s);
   if (e != hipSuccess) return e;
-  return hipLaunchKernel(f2, dim3((unsigned)(p.B * p.Hq)), dim3(128), args, 0, s);
+  return hipLaunchKernel(f2, dim3((unsigned)(p.B * p.Hq)), dim3(kMergeThreads), args, 0, s);
 }
 
 }  // namespace fa

@@ -22,19 +22,23 @@
 //   mask                 diagonal / tail tiles only.
 //   online softmax       running max m (base-2 units, scale*log2e folded into
 //                        one FMA), P = 2^(S*c - m) with v_exp_f32, running
-//                        sum l; the accumulator is rescaled only when some
-//                        row's maximum rose ([Evolution] §5, the exact case).
+//                        sum l of the fp32 probabilities.  The accumulator is
+//                        rescaled only when some row's maximum rose by more
+//                        than a threshold ([Evolution] §5 and [Comparison]
+//                        workarounds: conditional rescaling); the result is
+//                        exact for any reference maximum.
 //   O^T += V^T P^T       bf16 MFMA; the P^T registers are already the MFMA B
-//                        operand because V^T is stored in LDS with its keys
-//                        permuted to match (the contraction order is free).
+//                        operand (the contraction order over keys is free), and
+//                        the V^T A operand is read from the row-major V tile
+//                        with gfx950's transposing LDS load (ds_read_b64_tr_b16).
 // Normalisation by 1/l happens once at the end ([Evolution] §2 and §3), and
 // only O (bf16) and LSE (fp32) are written.
 //
-// K/V tiles are double-buffered in LDS: the global loads of tile j+1 are in
-// flight while tile j is computed, then written to the other buffer (the
-// CDNA counterpart of the Hopper asynchronous copies of [Evolution] §4).
-// Both LDS tiles use an XOR swizzle on 16-byte chunks so that the MFMA
-// operand reads of 16 consecutive rows hit distinct banks.
+// K/V tiles travel HBM -> LDS with direct-to-LDS loads (global_load_lds,
+// no register staging) into two LDS stages: tile j+1 is in flight while tile
+// j is computed (the CDNA counterpart of the asynchronous copies of
+// [Evolution] §4).  Both tiles use XOR swizzles on 16-byte chunks chosen so
+// that the MFMA operand reads spread over all LDS banks.
 
 #include "fa_internal.h"
 
@@ -42,6 +46,16 @@
 
 namespace fa {
 namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Rescale threshold in base-2 units: the running maximum (and with it the
+// accumulator) is only moved when some row's maximum rose by more than 8,
+// so probabilities stay below 2^8 between rescales.  Any reference maximum
+// gives the same exact result; this one only bounds the fp32/bf16 range.
+constexpr float kRescaleThreshold = 8.0f;
 
 template <int D, int BN, int NW>
 struct FwdShape {
@@ -51,67 +65,72 @@ struct FwdShape {
   static constexpr int KB = BN / 32;      // 32-key blocks per tile (S^T rows)
   static constexpr int DB = D / 32;       // 32-wide d blocks (O^T rows)
   static constexpr int KC = BN / 16;      // 16-key chunks (PV k-steps)
-  static constexpr int RBK = D * 2;       // bytes per K row in LDS
-  static constexpr int RBV = BN * 2;      // bytes per V^T row in LDS
-  static constexpr int KT_BYTES = BN * RBK;
-  static constexpr int VT_BYTES = D * RBV;
-  static constexpr int STAGE = KT_BYTES + VT_BYTES;
-  static constexpr int CPR = D / 8;       // 16-byte chunks per K/V row
-  static constexpr int K_CHUNKS = BN * CPR;
-  static constexpr int K_IT = (K_CHUNKS + NT - 1) / NT;
-  static constexpr int V_ASSIGN = (BN / 4) * CPR;   // (4-key group, d chunk)
-  static constexpr int V_IT = (V_ASSIGN + NT - 1) / NT;
+  static constexpr int RB = D * 2;        // bytes per K or V row in LDS
+  static constexpr int CPR = D / 8;       // 16-byte chunks per row
+  static constexpr int TILE = BN * RB;    // bytes of one K (or V) tile
+  static constexpr int STAGE = 2 * TILE;  // K tile then V tile
+  static constexpr int CHUNKS = BN * CPR;
+  static constexpr int LOADS = CHUNKS / (64 * NW);   // 1 KB wave loads per tile per wave
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
+  static_assert(CHUNKS % (64 * NW) == 0, "whole wave loads");
 };
 
-// Byte offset of 16-byte chunk c of row r in an LDS tile with RB-byte rows.
-// The XOR term differs for any 16 consecutive rows, so 16 lanes reading the
-// same logical chunk of consecutive rows touch 16 distinct bank groups.
+// LDS layouts (16-byte chunk c of row r is stored at chunk c ^ X(r)):
+//  K: X differs for any 16 consecutive rows, so the S^T A-operand reads (16
+//     lanes = 16 consecutive keys, same chunk) spread over all banks.
+//  V: X = 4*(r mod 4) (scaled for short rows), so the transposing reads of
+//     the PV A operand (8 consecutive keys x 4 consecutive chunks) hit every
+//     bank group exactly twice.
 template <int RB>
-__device__ __forceinline__ int swz(int r, int c) {
-  constexpr int NC = RB / 16;
-  int x;
-  if constexpr (RB >= 256) {
-    x = r & 15;
-  } else {
-    x = (r / (256 / RB)) & (NC - 1);
-  }
-  return r * RB + ((c ^ x) << 4);
+__device__ __forceinline__ int k_xor(int r) {
+  if constexpr (RB >= 256) return r & 15;
+  else return (r / (256 / RB)) & (RB / 16 - 1);
+}
+template <int RB>
+__device__ __forceinline__ int v_xor(int r) {
+  if constexpr (RB >= 256) return 4 * (r & 3);
+  else if constexpr (RB == 128) return 4 * ((r >> 1) & 1);
+  else return 0;
 }
 
-__device__ __forceinline__ float max_raw(float a, float b) { return a > b ? a : b; }
-
-// Combine a value with the same lane of the other 32-lane half.
 // The two results of the swap are the lane's own value and its partner's
 // (lane l and lane l ^ 32), in an order that depends on the half.
+__device__ __forceinline__ float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float half_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
-                                            __float_as_uint(x), false, false);
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ float half_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
-                                            __float_as_uint(x), false, false);
-  return max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-// Position of key kk (0..BN-1) inside a V^T row.  Within every 16 keys the
-// two middle bits are swapped: the PV B operand of lane half h, element
-// 4a+b (taken straight from the S^T accumulator) is key 8a+4h+b, and it must
-// meet V^T element 8h+4a+b of the A operand.
-__device__ __forceinline__ int vt_pos(int kk) {
-  const int g = (kk >> 2) & 3;
-  return (kk & ~15) | ((((g & 1) << 1) | (g >> 1)) << 2) | (kk & 3);
+// Issue the wave's share of one K or V tile as direct global -> LDS loads.
+// Wave load i writes 1 KB block (i*NW + wave) of the tile; lane l of that
+// load fetches the global chunk whose swizzled position is that block's l-th
+// chunk.  Rows past Nk re-read row Nk-1 (finite data; those keys are masked).
+template <int D, int BN, int NW, bool IS_V>
+__device__ __forceinline__ void load_tile(const uint16_t* base, int j0, int Nk, lds_char* tile,
+                                          int wave, int lane) {
+  using S = FwdShape<D, BN, NW>;
+#pragma unroll
+  for (int i = 0; i < S::LOADS; ++i) {
+    const int blk = i * NW + wave;
+    const int P = blk * 64 + lane;
+    const int row = P / S::CPR;
+    const int pc = P % S::CPR;
+    const int c = pc ^ (IS_V ? v_xor<S::RB>(row) : k_xor<S::RB>(row));
+    const int key = min(j0 + row, Nk - 1);
+    __builtin_amdgcn_global_load_lds(base + (size_t)key * D + c * 8, tile + blk * 1024, 16, 0, 0);
+  }
 }
 
 template <int D, int BN, int NW, bool CAUSAL>
-__device__ __forceinline__ void fwd_body(const FwdParams& p, char* smem) {
+__device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* stage0, lds_char* stage1) {
   using S = FwdShape<D, BN, NW>;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int hl = lane >> 5;   // lane half: selects k sub-block of MFMA operands
+  const int hl = lane >> 5;   // lane half: k sub-block of the MFMA operands
   const int n = lane & 31;    // query column of S^T / O^T owned by this lane
 
   // Grid: query block major (descending when causal, so the longest
@@ -138,109 +157,50 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, char* smem) {
     nkt = min(nkt, (last_row + off) / BN + 1);
   }
 
-  // Q rows of this wave as MFMA B operands: lane (h, n) holds
-  // Q[qw+n][16t + 8h .. +7] for k-step t.  Rows past Nq are zero.
+  // Q rows of this wave as MFMA B operands: lane (hl, n) holds
+  // Q[qw+n][16t + 8hl .. +7] for k-step t.  Rows past Nq are zero.
   bf16x8 qf[S::KSTEPS];
-  {
-    const int row = qw + n;
+  const int row = qw + n;
 #pragma unroll
-    for (int t = 0; t < S::KSTEPS; ++t) {
-      if (row < p.Nq) {
-        qf[t] = *reinterpret_cast<const bf16x8*>(qbase + (size_t)row * D + 16 * t + 8 * hl);
-      } else {
-        qf[t] = bf16x8{};
-      }
-    }
+  for (int t = 0; t < S::KSTEPS; ++t) {
+    qf[t] = row < p.Nq
+                ? *reinterpret_cast<const bf16x8*>(qbase + (size_t)row * D + 16 * t + 8 * hl)
+                : bf16x8{};
   }
 
-  // Register staging of one K/V tile (global -> VGPR -> LDS).
-  uint4 kst[S::K_IT];
-  uint4 vst[S::V_IT][4];
-
-  auto gload = [&](int j0) {
-#pragma unroll
-    for (int i = 0; i < S::K_IT; ++i) {
-      const int ci = tid + i * S::NT;
-      if (S::K_CHUNKS % S::NT == 0 || ci < S::K_CHUNKS) {
-        const int row = ci / S::CPR, c = ci % S::CPR;
-        const int key = j0 + row;
-        kst[i] = key < p.Nk
-                     ? *reinterpret_cast<const uint4*>(kbase + (size_t)key * D + c * 8)
-                     : make_uint4(0, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < S::V_IT; ++i) {
-      const int a = tid + i * S::NT;
-      if (S::V_ASSIGN % S::NT == 0 || a < S::V_ASSIGN) {
-        const int kg4 = a % (BN / 4), cd = a / (BN / 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = j0 + 4 * kg4 + r;
-          vst[i][r] = key < p.Nk
-                          ? *reinterpret_cast<const uint4*>(vbase + (size_t)key * D + cd * 8)
-                          : make_uint4(0, 0, 0, 0);
-        }
-      }
-    }
-  };
-
-  auto lstore = [&](char* st) {
-    char* sk = st;
-    char* sv = st + S::KT_BYTES;
-#pragma unroll
-    for (int i = 0; i < S::K_IT; ++i) {
-      const int ci = tid + i * S::NT;
-      if (S::K_CHUNKS % S::NT == 0 || ci < S::K_CHUNKS) {
-        const int row = ci / S::CPR, c = ci % S::CPR;
-        *reinterpret_cast<uint4*>(sk + swz<S::RBK>(row, c)) = kst[i];
-      }
-    }
-    // V^T: each thread transposes a 4-key x 8-d block into 8 rows of 4 keys.
-#pragma unroll
-    for (int i = 0; i < S::V_IT; ++i) {
-      const int a = tid + i * S::NT;
-      if (S::V_ASSIGN % S::NT == 0 || a < S::V_ASSIGN) {
-        const int kg4 = a % (BN / 4), cd = a / (BN / 4);
-        const int pos = vt_pos(4 * kg4);
-        const int chunk = pos >> 3, half = (pos >> 2) & 1;
-        const unsigned* w0 = reinterpret_cast<const unsigned*>(&vst[i][0]);
-        const unsigned* w1 = reinterpret_cast<const unsigned*>(&vst[i][1]);
-        const unsigned* w2 = reinterpret_cast<const unsigned*>(&vst[i][2]);
-        const unsigned* w3 = reinterpret_cast<const unsigned*>(&vst[i][3]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          const unsigned lo = __builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], sel);
-          const unsigned hi = __builtin_amdgcn_perm(w3[e >> 1], w2[e >> 1], sel);
-          *reinterpret_cast<uint2*>(sv + swz<S::RBV>(cd * 8 + e, chunk) + half * 8) =
-              make_uint2(lo, hi);
-        }
-      }
-    }
-  };
+  // Per-lane LDS offsets.  K: row n of each 32-key block, chunk (2t+hl)^X.
+  const int koff = n * S::RB;
+  const int kx = k_xor<S::RB>(n);
+  // V (transposing reads): 16-lane group G = lane/16 reads keys
+  // 4*hl + (j/4) (+16kc + 8a) at columns 32db + 16*(G&1) + 4*(j&3).
+  const int j16 = lane & 15;
+  const int vrow = 4 * hl + (j16 >> 2);
+  const int vx = v_xor<S::RB>(vrow) >> 2;
+  const int voff = vrow * S::RB + 32 * ((lane >> 4) & 1) + 16 * ((j16 & 3) >> 1) + 8 * (j16 & 1);
 
   f32x16 oacc[S::DB];
 #pragma unroll
   for (int db = 0; db < S::DB; ++db) oacc[db] = f32x16{};
   float m_run = -1e30f;   // finite, so 2^(m_old - m_new) is never inf - inf
   float l_run = 0.f;      // partial row sum over this lane half's keys
-  const int row = qw + n;
 
-  gload(0);
-  lstore(smem);
-  __syncthreads();
-
-  for (int j = 0; j < nkt; ++j) {
+  // One K/V tile step: prefetch tile j+1 into the other stage, compute tile
+  // j from this stage, then a barrier (which also waits for the prefetch).
+  // The two stages are distinct LDS arrays and the loop is unrolled by two,
+  // so the compiler can see that reads of `cur` never alias the in-flight
+  // direct-to-LDS writes of `nxt`.
+  auto step = [&](lds_char* cur, lds_char* nxt, int j) {
     const int j0 = j * BN;
-    const bool more = j + 1 < nkt;
-    if (more) gload(j0 + BN);
+    if (j + 1 < nkt) {
+      load_tile<D, BN, NW, false>(kbase, j0 + BN, p.Nk, nxt, wave, lane);
+      load_tile<D, BN, NW, true>(vbase, j0 + BN, p.Nk, nxt + S::TILE, wave, lane);
+    }
 
     bool active = qw < p.Nq;
     if (CAUSAL) active = active && (j0 <= qw + 31 + off);
     if (active) {
-      const char* sk = smem + (j & 1) * S::STAGE;
-      const char* sv = sk + S::KT_BYTES;
+      const lds_char* kt = cur;
+      const lds_char* vt = cur + S::TILE;
 
       // S^T = K Q^T
       f32x16 sacc[S::KB];
@@ -249,24 +209,21 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, char* smem) {
         sacc[kb] = f32x16{};
 #pragma unroll
         for (int t = 0; t < S::KSTEPS; ++t) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(sk + swz<S::RBK>(32 * kb + n, 2 * t + hl));
+          const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(
+              kt + kb * 32 * S::RB + koff + (((2 * t + hl) ^ kx) << 4));
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], sacc[kb], 0, 0, 0);
         }
       }
 
-      // Mask keys past Nk and, when causal, past the diagonal.
-      const bool need_mask = (j0 + BN > p.Nk) || (CAUSAL && j0 + BN - 1 > qw + off);
-      if (need_mask) {
-        const int lim = CAUSAL ? min(p.Nk - 1, row + off) : p.Nk - 1;
+      // Mask keys past Nk and, when causal, past the diagonal (tiles that
+      // need it only; the condition is uniform across the wave).
+      if ((j0 + BN > p.Nk) || (CAUSAL && j0 + BN - 1 > qw + off)) {
+        const int lim = (CAUSAL ? min(p.Nk - 1, row + off) : p.Nk - 1) - j0 - 4 * hl;
 #pragma unroll
-        for (int kb = 0; kb < S::KB; ++kb) {
+        for (int kb = 0; kb < S::KB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if (key > lim) sacc[kb][r] = -INFINITY;
-          }
-        }
+          for (int r = 0; r < 16; ++r)
+            if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
       }
 
       // Online softmax in base-2 units.
@@ -274,10 +231,10 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, char* smem) {
 #pragma unroll
       for (int kb = 0; kb < S::KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = max_raw(mx, sacc[kb][r]);
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[kb][r], sacc[kb][r + 1]));
       mx = half_max(mx);
-      const float m_new = max_raw(m_run, mx * p.c);
-      if (__any(m_new > m_run)) {
+      const float m_new = fmaxf(m_run, mx * p.c);
+      if (__any(m_new > m_run + kRescaleThreshold)) {
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
@@ -287,37 +244,50 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, char* smem) {
         m_run = m_new;
       }
       const float nm = -m_run;
-      float ls = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < S::KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.c, nm));
-          sacc[kb][r] = e;
-          ls += e;
-        }
-      l_run += ls;
 
       // P^T as bf16 B operands: chunk kc = registers 8*(kc%2).. of block kc/2.
+      // The row sum adds the fp32 probabilities: summing their bf16 roundings
+      // would put up to 2^-9 relative error into the LSE of short rows.
       bf16x8 pb[S::KC];
+      float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-      for (int kc = 0; kc < S::KC; ++kc)
+      for (int kc = 0; kc < S::KC; ++kc) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pb[kc][i] = (__bf16)sacc[kc >> 1][8 * (kc & 1) + i];
+        for (int i = 0; i < 8; i += 2) {
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kc >> 1][8 * (kc & 1) + i], p.c, nm));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kc >> 1][8 * (kc & 1) + i + 1], p.c, nm));
+          ls0 += e0;
+          ls1 += e1;
+          pb[kc][i] = (__bf16)e0;
+          pb[kc][i + 1] = (__bf16)e1;
+        }
+      }
+      l_run += ls0 + ls1;
 
-      // O^T += V^T P^T
+      // O^T += V^T P^T; the V^T operand comes from two transposing reads.
 #pragma unroll
-      for (int db = 0; db < S::DB; ++db)
+      for (int db = 0; db < S::DB; ++db) {
+        const int dbo = voff + 64 * (db ^ vx);
 #pragma unroll
         for (int kc = 0; kc < S::KC; ++kc) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(sv + swz<S::RBV>(32 * db + n, 2 * kc + hl));
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vt + dbo + (16 * kc) * S::RB));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vt + dbo + (16 * kc + 8) * S::RB));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc], oacc[db], 0, 0, 0);
         }
+      }
     }
-
-    if (more) lstore(smem + ((j + 1) & 1) * S::STAGE);
     __syncthreads();
+  };
+
+  load_tile<D, BN, NW, false>(kbase, 0, p.Nk, stage0, wave, lane);
+  load_tile<D, BN, NW, true>(vbase, 0, p.Nk, stage0 + S::TILE, wave, lane);
+  __syncthreads();
+  for (int j = 0; j < nkt; j += 2) {
+    step(stage0, stage1, j);
+    if (j + 1 < nkt) step(stage1, stage0, j + 1);
   }
 
   // Epilogue: O = acc / l (bf16, round to nearest even), LSE in natural log.
@@ -348,8 +318,9 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, char* smem) {
 #define FA_FWD_KERNEL(NAME, D, BN, NW, CAUSAL, WAVES_PER_EU)                          \
   extern "C" __global__ void __launch_bounds__(64 * NW, WAVES_PER_EU) NAME(           \
       fa::FwdParams p) {                                                              \
-    __shared__ __attribute__((aligned(16))) char smem[2 * fa::FwdShape<D, BN, NW>::STAGE]; \
-    fa::fwd_body<D, BN, NW, CAUSAL>(p, smem);                                         \
+    __shared__ __attribute__((aligned(1024))) char st0[fa::FwdShape<D, BN, NW>::STAGE];  \
+    __shared__ __attribute__((aligned(1024))) char st1[fa::FwdShape<D, BN, NW>::STAGE];  \
+    fa::fwd_body<D, BN, NW, CAUSAL>(p, (fa::lds_char*)st0, (fa::lds_char*)st1);        \
   }
 
 FA_FWD_KERNEL(fa_fwd_d32_nomask, 32, 64, 4, false, 2)
