@@ -125,7 +125,8 @@ __device__ __forceinline__ void load_tile(const uint16_t* base, int j0, int Nk, 
 }
 
 template <int D, int BN, int NW, bool CAUSAL>
-__device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* stage0, lds_char* stage1) {
+__device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_char* kb1,
+                                         lds_char* vb0, lds_char* vb1) {
   using S = FwdShape<D, BN, NW>;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -184,110 +185,128 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* stage0, l
   float m_run = -1e30f;   // finite, so 2^(m_old - m_new) is never inf - inf
   float l_run = 0.f;      // partial row sum over this lane half's keys
 
-  // One K/V tile step: prefetch tile j+1 into the other stage, compute tile
-  // j from this stage, then a barrier (which also waits for the prefetch).
-  // The two stages are distinct LDS arrays and the loop is unrolled by two,
-  // so the compiler can see that reads of `cur` never alias the in-flight
-  // direct-to-LDS writes of `nxt`.
-  auto step = [&](lds_char* cur, lds_char* nxt, int j) {
-    const int j0 = j * BN;
-    if (j + 1 < nkt) {
-      load_tile<D, BN, NW, false>(kbase, j0 + BN, p.Nk, nxt, wave, lane);
-      load_tile<D, BN, NW, true>(vbase, j0 + BN, p.Nk, nxt + S::TILE, wave, lane);
+  // S^T = K Q^T for one tile.
+  auto s_tile = [&](const lds_char* kt, f32x16 (&sacc)[S::KB]) {
+#pragma unroll
+    for (int kb = 0; kb < S::KB; ++kb) {
+      sacc[kb] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < S::KSTEPS; ++t) {
+        const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(
+            kt + kb * 32 * S::RB + koff + (((2 * t + hl) ^ kx) << 4));
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], sacc[kb], 0, 0, 0);
+      }
     }
+  };
 
-    bool active = qw < p.Nq;
-    if (CAUSAL) active = active && (j0 <= qw + 31 + off);
-    if (active) {
-      const lds_char* kt = cur;
-      const lds_char* vt = cur + S::TILE;
+  // Scores of tile t that a row may not see (past Nk, or past the diagonal
+  // when causal) become -inf.  Only tiles at the diagonal or the tail need
+  // it; the condition is uniform across the wave.
+  auto needs_mask = [&](int t) {
+    const int t0 = t * BN;
+    return (t0 + BN > p.Nk) || (CAUSAL && t0 + BN - 1 > qw + off);
+  };
+  auto mask_tile = [&](f32x16 (&sacc)[S::KB], int t) {
+    const int lim = (CAUSAL ? min(p.Nk - 1, row + off) : p.Nk - 1) - t * BN - 4 * hl;
+#pragma unroll
+    for (int kb = 0; kb < S::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
+  };
+  // Row maximum of a tile in base-2 units, combined over the lane halves.
+  auto tile_max = [&](const f32x16 (&sacc)[S::KB]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < S::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[kb][r], sacc[kb][r + 1]));
+    return half_max(mx) * p.c;
+  };
 
-      // S^T = K Q^T
-      f32x16 sacc[S::KB];
+  // One pipelined step for KV tile j.  On entry sc holds S^T of tile j and
+  // mnext its unmasked row maximum; LDS holds K_{j+1} (kr) and V_j (vr).  A
+  // tile at the diagonal or the tail is masked first and its maximum
+  // recomputed.  The step then moves the running maximum if it must,
+  // prefetches K_{j+2} into kw and V_{j+1} into vw, computes S^T of tile j+1
+  // into sn on the MFMA pipe while the VALU turns tile j's scores into
+  // probabilities and adds P_j V_j, and ends with the row maximum of tile
+  // j+1, which overlaps the last PV products.  Tiles a wave does not need
+  // (past its diagonal, or past Nk) are fully masked, so the four waves run
+  // the same schedule.
+  float mnext;
+  auto step = [&](const lds_char* kr, const lds_char* vr, lds_char* kw, lds_char* vw,
+                  f32x16 (&sc)[S::KB], f32x16 (&sn)[S::KB], int j) {
+    const int j0 = j * BN;
+    if (needs_mask(j)) {
+      mask_tile(sc, j);
+      mnext = tile_max(sc);
+    }
+    const float m_new = fmaxf(m_run, mnext);
+    if (__any(m_new > m_run + kRescaleThreshold)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < S::KB; ++kb) {
-        sacc[kb] = f32x16{};
+      for (int db = 0; db < S::DB; ++db)
 #pragma unroll
-        for (int t = 0; t < S::KSTEPS; ++t) {
-          const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(
-              kt + kb * 32 * S::RB + koff + (((2 * t + hl) ^ kx) << 4));
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], sacc[kb], 0, 0, 0);
-        }
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m_run = m_new;
+    }
+    if (j + 2 < nkt) load_tile<D, BN, NW, false>(kbase, j0 + 2 * BN, p.Nk, kw, wave, lane);
+    if (j + 1 < nkt) load_tile<D, BN, NW, true>(vbase, j0 + BN, p.Nk, vw, wave, lane);
+
+    // S^T of tile j+1 (its result is unused after the last tile).
+    s_tile(kr, sn);
+
+    // Per 16-key chunk kc: probabilities P = 2^(S*c - m) become the bf16 B
+    // operand (registers 8*(kc%2).. of block kc/2), then O^T += V^T P^T for
+    // every d block, the V^T operand coming from two transposing reads.  The
+    // row sum adds the fp32 probabilities: summing their bf16 roundings would
+    // put up to 2^-9 relative error into the LSE of short rows.
+    const float nm = -m_run;
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < S::KC; ++kc) {
+      bf16x8 pb;
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[kc >> 1][8 * (kc & 1) + i], p.c, nm));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[kc >> 1][8 * (kc & 1) + i + 1], p.c, nm));
+        ls0 += e0;
+        ls1 += e1;
+        pb[i] = (__bf16)e0;
+        pb[i + 1] = (__bf16)e1;
       }
-
-      // Mask keys past Nk and, when causal, past the diagonal (tiles that
-      // need it only; the condition is uniform across the wave).
-      if ((j0 + BN > p.Nk) || (CAUSAL && j0 + BN - 1 > qw + off)) {
-        const int lim = (CAUSAL ? min(p.Nk - 1, row + off) : p.Nk - 1) - j0 - 4 * hl;
-#pragma unroll
-        for (int kb = 0; kb < S::KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
-      }
-
-      // Online softmax in base-2 units.
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < S::KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[kb][r], sacc[kb][r + 1]));
-      mx = half_max(mx);
-      const float m_new = fmaxf(m_run, mx * p.c);
-      if (__any(m_new > m_run + kRescaleThreshold)) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < S::DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        m_run = m_new;
-      }
-      const float nm = -m_run;
-
-      // P^T as bf16 B operands: chunk kc = registers 8*(kc%2).. of block kc/2.
-      // The row sum adds the fp32 probabilities: summing their bf16 roundings
-      // would put up to 2^-9 relative error into the LSE of short rows.
-      bf16x8 pb[S::KC];
-      float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-      for (int kc = 0; kc < S::KC; ++kc) {
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kc >> 1][8 * (kc & 1) + i], p.c, nm));
-          const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kc >> 1][8 * (kc & 1) + i + 1], p.c, nm));
-          ls0 += e0;
-          ls1 += e1;
-          pb[kc][i] = (__bf16)e0;
-          pb[kc][i + 1] = (__bf16)e1;
-        }
-      }
-      l_run += ls0 + ls1;
-
-      // O^T += V^T P^T; the V^T operand comes from two transposing reads.
 #pragma unroll
       for (int db = 0; db < S::DB; ++db) {
-        const int dbo = voff + 64 * (db ^ vx);
-#pragma unroll
-        for (int kc = 0; kc < S::KC; ++kc) {
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vt + dbo + (16 * kc) * S::RB));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vt + dbo + (16 * kc + 8) * S::RB));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc], oacc[db], 0, 0, 0);
-        }
+        const int dbo = voff + 64 * (db ^ vx) + 16 * kc * S::RB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vr + dbo));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vr + dbo + 8 * S::RB));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
       }
     }
+    l_run += ls0 + ls1;
+
+    mnext = tile_max(sn);
     __syncthreads();
   };
 
-  load_tile<D, BN, NW, false>(kbase, 0, p.Nk, stage0, wave, lane);
-  load_tile<D, BN, NW, true>(vbase, 0, p.Nk, stage0 + S::TILE, wave, lane);
+  // Prologue: K_0, V_0, K_1 to LDS, S^T of tile 0 and its row maximum, then
+  // a barrier so that the first step may overwrite K_0's buffer.
+  f32x16 sa[S::KB], sb[S::KB];
+  load_tile<D, BN, NW, false>(kbase, 0, p.Nk, kb0, wave, lane);
+  load_tile<D, BN, NW, true>(vbase, 0, p.Nk, vb0, wave, lane);
+  if (nkt > 1) load_tile<D, BN, NW, false>(kbase, BN, p.Nk, kb1, wave, lane);
+  __syncthreads();
+  s_tile(kb0, sa);
+  mnext = tile_max(sa);
   __syncthreads();
   for (int j = 0; j < nkt; j += 2) {
-    step(stage0, stage1, j);
-    if (j + 1 < nkt) step(stage1, stage0, j + 1);
+    step(kb1, vb0, kb0, vb1, sa, sb, j);
+    if (j + 1 < nkt) step(kb0, vb1, kb1, vb0, sb, sa, j + 1);
   }
 
   // Epilogue: O = acc / l (bf16, round to nearest even), LSE in natural log.
@@ -318,9 +337,12 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* stage0, l
 #define FA_FWD_KERNEL(NAME, D, BN, NW, CAUSAL, WAVES_PER_EU)                          \
   extern "C" __global__ void __launch_bounds__(64 * NW, WAVES_PER_EU) NAME(           \
       fa::FwdParams p) {                                                              \
-    __shared__ __attribute__((aligned(1024))) char st0[fa::FwdShape<D, BN, NW>::STAGE];  \
-    __shared__ __attribute__((aligned(1024))) char st1[fa::FwdShape<D, BN, NW>::STAGE];  \
-    fa::fwd_body<D, BN, NW, CAUSAL>(p, (fa::lds_char*)st0, (fa::lds_char*)st1);        \
+    __shared__ __attribute__((aligned(1024))) char k0[fa::FwdShape<D, BN, NW>::TILE];    \
+    __shared__ __attribute__((aligned(1024))) char k1[fa::FwdShape<D, BN, NW>::TILE];    \
+    __shared__ __attribute__((aligned(1024))) char v0[fa::FwdShape<D, BN, NW>::TILE];    \
+    __shared__ __attribute__((aligned(1024))) char v1[fa::FwdShape<D, BN, NW>::TILE];    \
+    fa::fwd_body<D, BN, NW, CAUSAL>(p, (fa::lds_char*)k0, (fa::lds_char*)k1,             \
+                                    (fa::lds_char*)v0, (fa::lds_char*)v1);              \
   }
 
 FA_FWD_KERNEL(fa_fwd_d32_nomask, 32, 64, 4, false, 2)
