@@ -61,7 +61,7 @@ def _traffic(kernel, source_files):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline_fwd(cfg, qb, kb, vb, rows_per_head=512, heads=16):
+def cpu_baseline_fwd(cfg, qb, kb, vb, rows_per_head=4096, heads=32):
     """Oracle on `heads` heads x `rows_per_head` seeded rows of the prefill
     workload; throughput counts the algorithmic (causal) flop of those rows."""
     import oracle
@@ -82,7 +82,7 @@ def cpu_baseline_fwd(cfg, qb, kb, vb, rows_per_head=512, heads=16):
                        f"prefill, scores materialised then masked")
 
 
-def cpu_baseline_decode(cfg, qb, kb, vb, batches=2):
+def cpu_baseline_decode(cfg, qb, kb, vb, batches=8):
     import oracle
     q = datagen.f64_from_bf16_bits(qb[:batches])
     k = datagen.f64_from_bf16_bits(kb[:batches])

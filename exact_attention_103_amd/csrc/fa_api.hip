@@ -118,8 +118,8 @@ int fa_decode_num_splits(int B, int Hq, int Hkv, int Nk, int d) {
   const int group = Hq / Hkv;
   const int64_t per_split = checked_product({B, Hkv, group / fa::decode_group_tile(group)});
   if (per_split < 0) return FA_ERR_TOO_LARGE;
-  // About 2048 workgroups (8 per CU on 256 CUs), chunks of >= 256 keys.
-  int64_t s = (2048 + per_split - 1) / per_split;
+  // About 1024 workgroups (4 per CU on 256 CUs), chunks of >= 256 keys.
+  int64_t s = (1024 + per_split - 1) / per_split;
   const int64_t by_len = Nk / 256 > 0 ? Nk / 256 : 1;
   if (s > by_len) s = by_len;
   if (s > max_splits(Nk)) s = max_splits(Nk);

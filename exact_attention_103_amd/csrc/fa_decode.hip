@@ -7,23 +7,26 @@
 // Decode has one query row per sequence, so query-side parallelism gives
 // almost no work; the key/value sequence is cut into chunks instead and each
 // chunk becomes an independent workgroup ([Evolution] §6).  A workgroup owns
-// (batch b, KV head, chunk s) and all GT query heads that read that KV head,
-// so every K/V byte of the cache is read from HBM once.  It writes the
-// chunk's normalised partial output and LSE; a second kernel merges the
-// chunks with the log-sum-exp identity ([Evolution] §6, final reduction).
+// (batch b, KV head, chunk s) and the GT query heads that read that KV head
+// (up to 16), so every K/V byte of the cache is read from HBM once.  It
+// writes the chunk's normalised partial output and LSE; a second kernel
+// merges the chunks with the log-sum-exp identity ([Evolution] §6, final
+// reduction).
 //
-// The path is bandwidth bound (about 4 flop per K/V byte at GT = 4), so the
-// scores and the PV product use v_dot2_f32_bf16 on packed bf16 pairs rather
-// than MFMA, and the design goal is many 16-byte loads in flight:
-//   * LPK = d/8 lanes hold one key row (16 bytes each), so one wave-wide load
-//     instruction reads 64*16 contiguous bytes (64/LPK whole key rows);
-//   * each wave keeps U such loads of K and U of V in flight per iteration;
-//   * a dot product is reduced over its LPK lanes with DPP row operations.
-// Each group of LPK lanes keeps its own online-softmax state (running max m
-// in base-2 units, running sum l, unnormalised accumulator) over the keys it
-// saw; at the end of the chunk the lane groups of a wave are merged with
-// shuffles and the waves through LDS, with the same identity the merge
-// kernel uses.
+// The path is bandwidth bound (about 4 flop per K/V byte at GT = 4); the
+// arithmetic runs on the matrix cores so that the VALU stays light and the
+// waves can keep many loads in flight:
+//   * each wave streams its own 16-key tiles (tiles wave, wave+4, ... of the
+//     chunk), two tiles ahead;
+//   * K goes HBM -> VGPRs directly in the layout of the A operand of
+//     S^T = K Q^T (v_mfma_f32_16x16x32_bf16; columns = the GT query heads);
+//   * V goes HBM -> LDS with direct-to-LDS loads and feeds O^T += V^T P^T
+//     (v_mfma_f32_16x16x16_bf16) through the transposing LDS read; the P^T
+//     operand is the S^T accumulator converted to bf16 in place.
+// Online softmax per query head in base-2 units (running max, running sum,
+// unnormalised accumulator), with the accumulator rescaled only when a
+// maximum rises by more than 2^8.  At the end of the chunk the four waves'
+// states are merged through LDS with the same identity the merge kernel uses.
 
 #include "fa_internal.h"
 
@@ -32,60 +35,62 @@
 namespace fa {
 namespace {
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
-constexpr int kDecUnroll = 8;   // wave-wide K loads (and V loads) in flight per iteration
+constexpr int kDecTile = 16;                 // keys per wave tile
+constexpr float kDecRescaleThreshold = 8.0f;
 
 __device__ __forceinline__ float max_raw(float a, float b) { return a > b ? a : b; }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over groups of LPK consecutive lanes; every lane of a group ends with
-// the group total.  Pairs, quads, halves of a 16-lane row, whole rows, then
-// the two rows of a 32-lane half.
-template <int LPK>
-__device__ __forceinline__ float group_sum(float x) {
-  if constexpr (LPK >= 2) x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]
-  if constexpr (LPK >= 4) x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]
-  if constexpr (LPK >= 8) x += dpp<0x141>(x);   // row_half_mirror
-  if constexpr (LPK >= 16) x += dpp<0x140>(x);  // row_mirror
-  if constexpr (LPK >= 32) x += __shfl_xor(x, 16);
-  return x;
-}
-
-__device__ __forceinline__ float dot2(unsigned a, unsigned b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
-                                         __builtin_bit_cast(bf16x2, b), c, false);
-}
-
-__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
-  bf16x2 v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(unsigned, v);
-}
-
-template <int D, int GT>
+template <int D>
 struct DecShape {
-  static constexpr int LPK = D / 8;            // lanes per key row
-  static constexpr int KPI = 64 / LPK;         // key rows per wave-wide load
-  static constexpr int U = kDecUnroll;
-  static constexpr int KEYS_WAVE = U * KPI;    // keys per wave per iteration
-  static constexpr int KEYS_ITER = kDecWaves * KEYS_WAVE;
-  static constexpr int NPART = kDecWaves;       // partial states merged through LDS
-  static constexpr int LDS_ACC = NPART * GT * D; // floats
-  static_assert(U % 2 == 0, "PV consumes key pairs");
+  static constexpr int RB = D * 2;                       // bytes per V row in LDS
+  static constexpr int CPR = D / 8;                      // 16-byte chunks per row
+  static constexpr int VTILE = kDecTile * RB;            // bytes of one V tile
+  static constexpr int VLOADS = kDecTile * CPR / 64;     // 1 KB wave loads per V tile
+  static constexpr int KSTEPS = D / 32;                  // S^T k-steps
+  static constexpr int NDB = D / 16;                     // 16-row d blocks of O^T
+  static_assert(VLOADS >= 1, "tile shape");
 };
 
+// V tile swizzle: 16-byte chunk c of row r sits at c ^ X(r).  The PV operand
+// reads take chunks 2db, 2db+1 of all 16 rows; X spreads them so that every
+// bank group is hit exactly twice (scaled for rows shorter than 256 bytes).
+template <int RB>
+__device__ __forceinline__ int dv_xor(int r) {
+  if constexpr (RB >= 256) return 2 * (r & 7);
+  else if constexpr (RB == 128) return 2 * ((r >> 1) & 3);
+  else return 2 * ((r >> 2) & 1);
+}
+
+// Reductions over the four 16-lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float group4_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group4_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int D, int GT>
-__device__ __forceinline__ void decode_split_body(const DecodeParams& p, float* lds) {
-  using S = DecShape<D, GT>;
+__device__ __forceinline__ void decode_split_body(const DecodeParams& p, lds_char* vs0,
+                                                  lds_char* vs1, float* mlds) {
+  using S = DecShape<D>;
+  static_assert(GT >= 1 && GT <= 16, "query heads per workgroup");
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int ks = lane / S::LPK;   // key slot inside one wave-wide load
-  const int c = lane % S::LPK;    // 16-byte chunk of the row: d = 8c .. 8c+7
+  const int col = lane & 15;   // MFMA column: query head h0 + col
+  const int grp = lane >> 4;   // 16-lane group: k sub-block / row block
 
   // Workgroup -> (b, kv head, split, head group); head group innermost so
   // workgroups that share K/V bytes run next to each other.
@@ -99,148 +104,133 @@ __device__ __forceinline__ void decode_split_body(const DecodeParams& p, float* 
 
   const int kbeg = s * p.chunk;
   const int kend = min(kbeg + p.chunk, p.Nk);
+  const int ntiles = kend > kbeg ? (kend - kbeg + kDecTile - 1) / kDecTile : 0;
+  const int my = ntiles > wave ? (ntiles - wave + kDecWaves - 1) / kDecWaves : 0;
 
-  // Queries: 8 bf16 per lane per head, as 4 packed pairs.
-  unsigned qw[GT][4];
+  // Q^T as the B operand: lane (grp, col) holds Q[h0+col][32t + 8grp .. +7].
+  bf16x8 qf[S::KSTEPS];
 #pragma unroll
-  for (int gq = 0; gq < GT; ++gq) {
-    const uint4 t = *reinterpret_cast<const uint4*>(
-        p.q + ((size_t)(b * p.Hq + h0 + gq)) * D + 8 * c);
-    qw[gq][0] = t.x; qw[gq][1] = t.y; qw[gq][2] = t.z; qw[gq][3] = t.w;
-  }
-
-  float m[GT], l[GT], acc[GT][8];
-#pragma unroll
-  for (int gq = 0; gq < GT; ++gq) {
-    m[gq] = -1e30f;
-    l[gq] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[gq][e] = 0.f;
+  for (int t = 0; t < S::KSTEPS; ++t) {
+    qf[t] = col < GT ? *reinterpret_cast<const bf16x8*>(
+                           p.q + ((size_t)(b * p.Hq + h0 + col)) * D + 32 * t + 8 * grp)
+                     : bf16x8{};
   }
 
   const size_t kvoff = ((size_t)(b * p.Hkv + kvh)) * p.Nk * D;
   const uint16_t* kb = p.k + kvoff;
   const uint16_t* vb = p.v + kvoff;
+  lds_char* v0 = vs0 + wave * S::VTILE;
+  lds_char* v1 = vs1 + wave * S::VTILE;
 
-  for (int base = kbeg + wave * S::KEYS_WAVE; base < kend; base += S::KEYS_ITER) {
-    uint4 kv[S::U], vv[S::U];
+  // Transposing-read offsets: lane j of group grp addresses row 4*grp + j/4,
+  // columns 16db + 4*(j&3), so it receives V[4grp + k][16db + j] for k = 0..3.
+  const int vrow = 4 * grp + (col >> 2);
+  const int vx = dv_xor<S::RB>(vrow) >> 1;
+  const int voff = vrow * S::RB + 16 * ((col & 3) >> 1) + 8 * (col & 1);
+
+  // Issue the loads of this wave's i-th tile: K rows into registers (A
+  // operand layout: lane (grp, col) takes key col, d = 32t + 8grp ..), V rows
+  // into LDS.  Keys past the chunk end re-read its last key (masked later).
+  auto issue = [&](int i, bf16x8 (&kf)[S::KSTEPS], lds_char* vt) {
+    const int tb = kbeg + kDecTile * (wave + kDecWaves * i);
+    const int key = min(tb + col, kend - 1);
 #pragma unroll
-    for (int u = 0; u < S::U; ++u) {
-      const int key = base + u * S::KPI + ks;
-      if (key < kend) {
-        kv[u] = *reinterpret_cast<const uint4*>(kb + (size_t)key * D + 8 * c);
-        vv[u] = *reinterpret_cast<const uint4*>(vb + (size_t)key * D + 8 * c);
-      } else {
-        kv[u] = make_uint4(0, 0, 0, 0);
-        vv[u] = make_uint4(0, 0, 0, 0);
-      }
+    for (int t = 0; t < S::KSTEPS; ++t)
+      kf[t] = *reinterpret_cast<const bf16x8*>(kb + (size_t)key * D + 32 * t + 8 * grp);
+#pragma unroll
+    for (int L = 0; L < S::VLOADS; ++L) {
+      const int P = L * 64 + lane;
+      const int row = P / S::CPR;
+      const int c = (P % S::CPR) ^ dv_xor<S::RB>(row);
+      const int vkey = min(tb + row, kend - 1);
+      __builtin_amdgcn_global_load_lds(vb + (size_t)vkey * D + c * 8, vt + L * 1024, 16, 0, 0);
     }
+  };
 
-    // Scores in base-2 units; keys past the chunk end are -inf.
-    float sc[S::U][GT];
+  float m = -1e30f;   // running max (base 2) of query h0+col, same in all lane groups
+  float l = 0.f;      // running sum over this lane group's keys
+  f32x4 oacc[S::NDB];
 #pragma unroll
-    for (int u = 0; u < S::U; ++u) {
-      const bool ok = base + u * S::KPI + ks < kend;
+  for (int db = 0; db < S::NDB; ++db) oacc[db] = f32x4{};
+
+  auto process = [&](int i, const bf16x8 (&kf)[S::KSTEPS], const lds_char* vt) {
+    const int tb = kbeg + kDecTile * (wave + kDecWaves * i);
+    // S^T: lane (grp, col) gets keys tb + 4grp + r (r = 0..3) of query col.
+    f32x4 sacc = f32x4{};
 #pragma unroll
-      for (int gq = 0; gq < GT; ++gq) {
-        float t = dot2(kv[u].x, qw[gq][0], 0.f);
-        t = dot2(kv[u].y, qw[gq][1], t);
-        t = dot2(kv[u].z, qw[gq][2], t);
-        t = dot2(kv[u].w, qw[gq][3], t);
-        t = group_sum<S::LPK>(t);
-        sc[u][gq] = ok ? t * p.c : -INFINITY;
-      }
+    for (int t = 0; t < S::KSTEPS; ++t)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t], qf[t], sacc, 0, 0, 0);
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      sv[r] = (tb + 4 * grp + r < kend) ? sacc[r] * p.c : -INFINITY;
+    const float mx = group4_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+    const float m_new = fmaxf(m, mx);
+    if (__any(m_new > m + kDecRescaleThreshold)) {
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < S::NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oacc[db][r] *= alpha;
+      m = m_new;
     }
-
-    // Online softmax update of this lane group's state.
+    float pr[4];
 #pragma unroll
-    for (int gq = 0; gq < GT; ++gq) {
-      float mx = sc[0][gq];
+    for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(sv[r] - m);
+    l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    const s16x4 pb = __builtin_bit_cast(s16x4, (bf16x4_t){(__bf16)pr[0], (__bf16)pr[1],
+                                                          (__bf16)pr[2], (__bf16)pr[3]});
+    // O^T += V^T P^T over the 16 keys of the tile.
 #pragma unroll
-      for (int u = 1; u < S::U; ++u) mx = max_raw(mx, sc[u][gq]);
-      const float m_new = max_raw(m[gq], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m[gq] - m_new);
-      m[gq] = m_new;
-      float ls = 0.f;
-#pragma unroll
-      for (int u = 0; u < S::U; ++u) {
-        sc[u][gq] = __builtin_amdgcn_exp2f(sc[u][gq] - m_new);
-        ls += sc[u][gq];
-      }
-      l[gq] = l[gq] * alpha + ls;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[gq][e] *= alpha;
+    for (int db = 0; db < S::NDB; ++db) {
+      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vt + voff + 32 * (db ^ vx)));
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, oacc[db], 0, 0, 0);
     }
+  };
 
-    // acc += P V over key pairs: (V[u][d], V[u+1][d]) . (p[u], p[u+1]).
-#pragma unroll
-    for (int u = 0; u < S::U; u += 2) {
-      const unsigned a[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
-      const unsigned bq[4] = {vv[u + 1].x, vv[u + 1].y, vv[u + 1].z, vv[u + 1].w};
-      unsigned x[8];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        x[2 * w] = __builtin_amdgcn_perm(bq[w], a[w], 0x05040100u);
-        x[2 * w + 1] = __builtin_amdgcn_perm(bq[w], a[w], 0x07060302u);
-      }
-#pragma unroll
-      for (int gq = 0; gq < GT; ++gq) {
-        const unsigned pp = pack_bf16(sc[u][gq], sc[u + 1][gq]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[gq][e] = dot2(x[e], pp, acc[gq][e]);
-      }
+  bf16x8 kf0[S::KSTEPS], kf1[S::KSTEPS];
+  if (my > 0) issue(0, kf0, v0);
+  if (my > 1) issue(1, kf1, v1);
+  for (int i = 0; i < my; i += 2) {
+    process(i, kf0, v0);
+    if (i + 2 < my) issue(i + 2, kf0, v0);
+    if (i + 1 < my) {
+      process(i + 1, kf1, v1);
+      if (i + 3 < my) issue(i + 3, kf1, v1);
     }
   }
 
-  // Merge the lane groups of each wave (same chunk c, different key slot)
-  // with shuffles, then the waves through LDS.
-#pragma unroll
-  for (int x = S::LPK; x < 64; x *= 2) {
-#pragma unroll
-    for (int gq = 0; gq < GT; ++gq) {
-      const float mo = __shfl_xor(m[gq], x);
-      const float lo = __shfl_xor(l[gq], x);
-      const float mn = max_raw(m[gq], mo);
-      const float ws = __builtin_amdgcn_exp2f(m[gq] - mn);
-      const float wo = __builtin_amdgcn_exp2f(mo - mn);
-      m[gq] = mn;
-      l[gq] = ws * l[gq] + wo * lo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[gq][e] = ws * acc[gq][e] + wo * __shfl_xor(acc[gq][e], x);
-    }
+  // Merge the four waves' states through LDS: lane (grp, col) owns O^T rows
+  // 16db + 4grp + r of query col.
+  const float lt = group4_sum(l);
+  float* sm_m = mlds;                            // [4][16]
+  float* sm_l = sm_m + kDecWaves * 16;           // [4][16]
+  float* sm_acc = sm_l + kDecWaves * 16;         // [4][16][D]
+  if (grp == 0) {
+    sm_m[wave * 16 + col] = m;
+    sm_l[wave * 16 + col] = lt;
   }
-  float* sm_m = lds;                              // [NPART][GT]
-  float* sm_l = sm_m + S::NPART * GT;             // [NPART][GT]
-  float* sm_acc = sm_l + S::NPART * GT;           // [NPART][GT][D]
-  if (ks == 0) {
-    if (c == 0) {
 #pragma unroll
-      for (int gq = 0; gq < GT; ++gq) {
-        sm_m[wave * GT + gq] = m[gq];
-        sm_l[wave * GT + gq] = l[gq];
-      }
-    }
-#pragma unroll
-    for (int gq = 0; gq < GT; ++gq) {
-      float4* dst = reinterpret_cast<float4*>(sm_acc + ((size_t)wave * GT + gq) * D + 8 * c);
-      dst[0] = make_float4(acc[gq][0], acc[gq][1], acc[gq][2], acc[gq][3]);
-      dst[1] = make_float4(acc[gq][4], acc[gq][5], acc[gq][6], acc[gq][7]);
-    }
-  }
+  for (int db = 0; db < S::NDB; ++db)
+    *reinterpret_cast<float4*>(sm_acc + ((size_t)wave * 16 + col) * D + 16 * db + 4 * grp) =
+        make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
   __syncthreads();
 
   for (int o = tid; o < GT * D; o += kDecThreads) {
     const int gq = o / D, dd = o % D;
     float M = -1e30f;
-    for (int i = 0; i < S::NPART; ++i) M = max_raw(M, sm_m[i * GT + gq]);
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) M = max_raw(M, sm_m[w * 16 + gq]);
     float W = 0.f, O = 0.f;
-    for (int i = 0; i < S::NPART; ++i) {
-      const float w = __builtin_amdgcn_exp2f(sm_m[i * GT + gq] - M);
-      W += w * sm_l[i * GT + gq];
-      O += w * sm_acc[((size_t)i * GT + gq) * D + dd];
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float wt = __builtin_amdgcn_exp2f(sm_m[w * 16 + gq] - M);
+      W += wt * sm_l[w * 16 + gq];
+      O += wt * sm_acc[((size_t)w * 16 + gq) * D + dd];
     }
-    const int hq = h0 + gq;
-    const size_t ps = ((size_t)(b * p.Hq + hq)) * p.splits + s;
+    const size_t ps = ((size_t)(b * p.Hq + h0 + gq)) * p.splits + s;
     if (W > 0.f) {
       p.o_part[ps * D + dd] = O / W;
       if (dd == 0) p.lse_part[ps] = (M + log2f(W)) * kLn2;
@@ -307,12 +297,13 @@ __device__ __forceinline__ void decode_merge_body(const DecodeParams& p) {
 }  // namespace
 }  // namespace fa
 
-#define FA_DEC_SPLIT(D, GT)                                                           \
-  extern "C" __global__ void __launch_bounds__(fa::kDecThreads)                       \
-      fa_decode_split_d##D##_g##GT(fa::DecodeParams p) {                             \
-    __shared__ __attribute__((aligned(16)))                                           \
-        float lds[2 * fa::DecShape<D, GT>::NPART * GT + fa::DecShape<D, GT>::LDS_ACC]; \
-    fa::decode_split_body<D, GT>(p, lds);                                             \
+#define FA_DEC_SPLIT(D, GT)                                                              \
+  extern "C" __global__ void __launch_bounds__(fa::kDecThreads, 2)                       \
+      fa_decode_split_d##D##_g##GT(fa::DecodeParams p) {                                \
+    __shared__ __attribute__((aligned(1024))) char vs0[fa::kDecWaves * fa::DecShape<D>::VTILE]; \
+    __shared__ __attribute__((aligned(1024))) char vs1[fa::kDecWaves * fa::DecShape<D>::VTILE]; \
+    __shared__ __attribute__((aligned(16))) float mlds[fa::kDecWaves * 16 * (2 + D)];   \
+    fa::decode_split_body<D, GT>(p, (fa::lds_char*)vs0, (fa::lds_char*)vs1, mlds);      \
   }
 
 #define FA_DEC_MERGE(D)                                                               \
@@ -321,8 +312,9 @@ __device__ __forceinline__ void decode_merge_body(const DecodeParams& p) {
     fa::decode_merge_body<D>(p);                                                      \
   }
 
-#define FA_DEC_ALL(D) \
-  FA_DEC_SPLIT(D, 1) FA_DEC_SPLIT(D, 2) FA_DEC_SPLIT(D, 4) FA_DEC_SPLIT(D, 8) FA_DEC_MERGE(D)
+#define FA_DEC_ALL(D)                                                                  \
+  FA_DEC_SPLIT(D, 1) FA_DEC_SPLIT(D, 2) FA_DEC_SPLIT(D, 4) FA_DEC_SPLIT(D, 8)          \
+  FA_DEC_SPLIT(D, 16) FA_DEC_MERGE(D)
 
 FA_DEC_ALL(32)
 FA_DEC_ALL(64)
@@ -332,6 +324,7 @@ FA_DEC_ALL(256)
 namespace fa {
 
 int decode_group_tile(int group) {
+  if (group % 16 == 0) return 16;
   if (group % 8 == 0) return 8;
   if (group % 4 == 0) return 4;
   if (group % 2 == 0) return 2;
@@ -348,6 +341,7 @@ const void* split_fn(int d, int gt) {
       case 2: return (const void*)fa_decode_split_d##D##_g2;         \
       case 4: return (const void*)fa_decode_split_d##D##_g4;         \
       case 8: return (const void*)fa_decode_split_d##D##_g8;         \
+      case 16: return (const void*)fa_decode_split_d##D##_g16;       \
     }                                                                \
     return nullptr;
   switch (d) {
@@ -373,11 +367,15 @@ const void* merge_fn(int d) {
 }  // namespace
 
 const char* decode_kernel_name(int d, int group, int stage) {
-  static const char* const split_names[4][4] = {
-      {"fa_decode_split_d32_g1", "fa_decode_split_d32_g2", "fa_decode_split_d32_g4", "fa_decode_split_d32_g8"},
-      {"fa_decode_split_d64_g1", "fa_decode_split_d64_g2", "fa_decode_split_d64_g4", "fa_decode_split_d64_g8"},
-      {"fa_decode_split_d128_g1", "fa_decode_split_d128_g2", "fa_decode_split_d128_g4", "fa_decode_split_d128_g8"},
-      {"fa_decode_split_d256_g1", "fa_decode_split_d256_g2", "fa_decode_split_d256_g4", "fa_decode_split_d256_g8"}};
+  static const char* const split_names[4][5] = {
+      {"fa_decode_split_d32_g1", "fa_decode_split_d32_g2", "fa_decode_split_d32_g4",
+       "fa_decode_split_d32_g8", "fa_decode_split_d32_g16"},
+      {"fa_decode_split_d64_g1", "fa_decode_split_d64_g2", "fa_decode_split_d64_g4",
+       "fa_decode_split_d64_g8", "fa_decode_split_d64_g16"},
+      {"fa_decode_split_d128_g1", "fa_decode_split_d128_g2", "fa_decode_split_d128_g4",
+       "fa_decode_split_d128_g8", "fa_decode_split_d128_g16"},
+      {"fa_decode_split_d256_g1", "fa_decode_split_d256_g2", "fa_decode_split_d256_g4",
+       "fa_decode_split_d256_g8", "fa_decode_split_d256_g16"}};
   static const char* const merge_names[4] = {"fa_decode_merge_d32", "fa_decode_merge_d64",
                                              "fa_decode_merge_d128", "fa_decode_merge_d256"};
   int di;
@@ -392,7 +390,7 @@ const char* decode_kernel_name(int d, int group, int stage) {
   if (stage == 1) return merge_names[di];
   if (stage != 0) return nullptr;
   const int gt = decode_group_tile(group);
-  const int gi = gt == 1 ? 0 : gt == 2 ? 1 : gt == 4 ? 2 : 3;
+  const int gi = gt == 1 ? 0 : gt == 2 ? 1 : gt == 4 ? 2 : gt == 8 ? 3 : 4;
   return split_names[di][gi];
 }
 

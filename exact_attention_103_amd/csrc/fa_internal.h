@@ -56,8 +56,8 @@ const char* decode_kernel_name(int d, int group, int stage);
 struct FwdTile { int bm, bn, waves; };
 FwdTile fwd_tile(int d);
 
-// Query heads handled by one decode split workgroup: the largest of 8, 4, 2,
-// 1 that divides the number of query heads per KV head.
+// Query heads handled by one decode split workgroup: the largest of 16, 8,
+// 4, 2, 1 that divides the number of query heads per KV head.
 int decode_group_tile(int group);
 
 // Keys per decode split are rounded up to this multiple.

@@ -67,7 +67,8 @@ def test_kernel_names():
         assert fa.fa_decode_kernel_name(d, 4, 0) == f"fa_decode_split_d{d}_g4"
         assert fa.fa_decode_kernel_name(d, 6, 0) == f"fa_decode_split_d{d}_g2"
         assert fa.fa_decode_kernel_name(d, 3, 0) == f"fa_decode_split_d{d}_g1"
-        assert fa.fa_decode_kernel_name(d, 16, 0) == f"fa_decode_split_d{d}_g8"
+        assert fa.fa_decode_kernel_name(d, 16, 0) == f"fa_decode_split_d{d}_g16"
+        assert fa.fa_decode_kernel_name(d, 24, 0) == f"fa_decode_split_d{d}_g8"
         assert fa.fa_decode_kernel_name(d, 4, 1) == f"fa_decode_merge_d{d}"
     assert fa.fa_fwd_kernel_name(96, 0) is None
     assert fa.fa_fwd_kernel_name(128, 2) is None
@@ -82,8 +83,8 @@ def test_workspace_and_splits():
     assert fa.fa_decode_max_splits(32768) == 512
     assert fa.fa_decode_max_splits(1) == 1
     assert fa.fa_decode_max_splits(65) == 2
-    # The decode workload: 8 x 8 (b, KV head) pairs -> 32 splits of 1024 keys.
-    assert fa.fa_decode_num_splits(8, 32, 8, 32768, 128) == 32
+    # The decode workload: 8 x 8 (b, KV head) pairs -> 16 splits of 2048 keys.
+    assert fa.fa_decode_num_splits(8, 32, 8, 32768, 128) == 16
     for args in [(1, 1, 1, 1, 64), (1, 8, 1, 100000, 128), (64, 64, 8, 4096, 32),
                  (1, 6, 2, 777, 256)]:
         s = fa.fa_decode_num_splits(*args)
