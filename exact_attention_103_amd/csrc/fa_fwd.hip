@@ -57,9 +57,10 @@ typedef __attribute__((address_space(3))) char lds_char;
 // gives the same exact result; this one only bounds the fp32/bf16 range.
 constexpr float kRescaleThreshold = 8.0f;
 
-template <int D, int BN, int NW>
+template <int D, int BN, int NW, int NQB>
 struct FwdShape {
-  static constexpr int BM = 32 * NW;
+  static constexpr int RPW = 32 * NQB;    // query rows per wave
+  static constexpr int BM = RPW * NW;     // query rows per workgroup
   static constexpr int NT = 64 * NW;
   static constexpr int KSTEPS = D / 16;   // MFMA k-steps over d (S^T)
   static constexpr int KB = BN / 32;      // 32-key blocks per tile (S^T rows)
@@ -68,7 +69,6 @@ struct FwdShape {
   static constexpr int RB = D * 2;        // bytes per K or V row in LDS
   static constexpr int CPR = D / 8;       // 16-byte chunks per row
   static constexpr int TILE = BN * RB;    // bytes of one K (or V) tile
-  static constexpr int STAGE = 2 * TILE;  // K tile then V tile
   static constexpr int CHUNKS = BN * CPR;
   static constexpr int LOADS = CHUNKS / (64 * NW);   // 1 KB wave loads per tile per wave
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
@@ -111,7 +111,7 @@ __device__ __forceinline__ float half_sum(float x) {
 template <int D, int BN, int NW, bool IS_V>
 __device__ __forceinline__ void load_tile(const uint16_t* base, int j0, int Nk, lds_char* tile,
                                           int wave, int lane) {
-  using S = FwdShape<D, BN, NW>;
+  using S = FwdShape<D, BN, NW, 1>;
 #pragma unroll
   for (int i = 0; i < S::LOADS; ++i) {
     const int blk = i * NW + wave;
@@ -124,10 +124,13 @@ __device__ __forceinline__ void load_tile(const uint16_t* base, int j0, int Nk, 
   }
 }
 
-template <int D, int BN, int NW, bool CAUSAL>
+template <int D, int BN, int NW, int NQB, bool CAUSAL>
 __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_char* kb1,
                                          lds_char* vb0, lds_char* vb1) {
-  using S = FwdShape<D, BN, NW>;
+  using S = FwdShape<D, BN, NW, NQB>;
+  // Two S^T tiles live at once (next tile's QK^T overlapping this tile's
+  // softmax) only when they are small enough for two waves per SIMD.
+  constexpr bool kPipe = NQB == 1 && BN <= 64;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -145,8 +148,8 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
   const int h = bh - b * p.Hq;
   const int g = h / p.group;
   const int q0 = qblk * S::BM;
-  const int qw = q0 + 32 * wave;
-  const int off = p.Nk - p.Nq;   // key j allowed for row i iff j <= i + off
+  const int qw = q0 + S::RPW * wave;   // first query row of this wave
+  const int off = p.Nk - p.Nq;         // key j allowed for row i iff j <= i + off
 
   const uint16_t* qbase = p.q + (size_t)(b * p.Hq + h) * p.Nq * D;
   const uint16_t* kbase = p.k + (size_t)(b * p.Hkv + g) * p.Nk * D;
@@ -158,15 +161,20 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
     nkt = min(nkt, (last_row + off) / BN + 1);
   }
 
-  // Q rows of this wave as MFMA B operands: lane (hl, n) holds
-  // Q[qw+n][16t + 8hl .. +7] for k-step t.  Rows past Nq are zero.
-  bf16x8 qf[S::KSTEPS];
-  const int row = qw + n;
+  // The wave owns NQB blocks of 32 query rows; block qb is row qw+32qb+n of
+  // this lane.  Q of each block is an MFMA B operand: lane (hl, n) holds
+  // Q[row][16t + 8hl .. +7] for k-step t.  Rows past Nq are zero.
+  bf16x8 qf[NQB][S::KSTEPS];
+  int row[NQB];
 #pragma unroll
-  for (int t = 0; t < S::KSTEPS; ++t) {
-    qf[t] = row < p.Nq
-                ? *reinterpret_cast<const bf16x8*>(qbase + (size_t)row * D + 16 * t + 8 * hl)
-                : bf16x8{};
+  for (int qb = 0; qb < NQB; ++qb) {
+    row[qb] = qw + 32 * qb + n;
+#pragma unroll
+    for (int t = 0; t < S::KSTEPS; ++t) {
+      qf[qb][t] = row[qb] < p.Nq ? *reinterpret_cast<const bf16x8*>(
+                                       qbase + (size_t)row[qb] * D + 16 * t + 8 * hl)
+                                 : bf16x8{};
+    }
   }
 
   // Per-lane LDS offsets.  K: row n of each 32-key block, chunk (2t+hl)^X.
@@ -179,22 +187,29 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
   const int vx = v_xor<S::RB>(vrow) >> 2;
   const int voff = vrow * S::RB + 32 * ((lane >> 4) & 1) + 16 * ((j16 & 3) >> 1) + 8 * (j16 & 1);
 
-  f32x16 oacc[S::DB];
+  f32x16 oacc[NQB][S::DB];
+  float m_run[NQB], l_run[NQB];
 #pragma unroll
-  for (int db = 0; db < S::DB; ++db) oacc[db] = f32x16{};
-  float m_run = -1e30f;   // finite, so 2^(m_old - m_new) is never inf - inf
-  float l_run = 0.f;      // partial row sum over this lane half's keys
+  for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db) oacc[qb][db] = f32x16{};
+    m_run[qb] = -1e30f;   // finite, so 2^(m_old - m_new) is never inf - inf
+    l_run[qb] = 0.f;      // partial row sum over this lane half's keys
+  }
 
-  // S^T = K Q^T for one tile.
-  auto s_tile = [&](const lds_char* kt, f32x16 (&sacc)[S::KB]) {
+  // S^T = K Q^T for one tile; every K operand read from LDS feeds NQB MFMAs.
+  auto s_tile = [&](const lds_char* kt, f32x16 (&sacc)[NQB][S::KB]) {
 #pragma unroll
     for (int kb = 0; kb < S::KB; ++kb) {
-      sacc[kb] = f32x16{};
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) sacc[qb][kb] = f32x16{};
 #pragma unroll
       for (int t = 0; t < S::KSTEPS; ++t) {
         const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(
             kt + kb * 32 * S::RB + koff + (((2 * t + hl) ^ kx) << 4));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], sacc[kb], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][t], sacc[qb][kb], 0, 0, 0);
       }
     }
   };
@@ -206,22 +221,28 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
     const int t0 = t * BN;
     return (t0 + BN > p.Nk) || (CAUSAL && t0 + BN - 1 > qw + off);
   };
-  auto mask_tile = [&](f32x16 (&sacc)[S::KB], int t) {
-    const int lim = (CAUSAL ? min(p.Nk - 1, row + off) : p.Nk - 1) - t * BN - 4 * hl;
+  auto mask_tile = [&](f32x16 (&sacc)[NQB][S::KB], int t) {
 #pragma unroll
-    for (int kb = 0; kb < S::KB; ++kb)
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int lim = (CAUSAL ? min(p.Nk - 1, row[qb] + off) : p.Nk - 1) - t * BN - 4 * hl;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
+      for (int kb = 0; kb < S::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[qb][kb][r] = -INFINITY;
+    }
   };
   // Row maximum of a tile in base-2 units, combined over the lane halves.
-  auto tile_max = [&](const f32x16 (&sacc)[S::KB]) {
-    float mx = -INFINITY;
+  auto tile_max = [&](const f32x16 (&sacc)[NQB][S::KB], float (&mx)[NQB]) {
 #pragma unroll
-    for (int kb = 0; kb < S::KB; ++kb)
+    for (int qb = 0; qb < NQB; ++qb) {
+      float x = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[kb][r], sacc[kb][r + 1]));
-    return half_max(mx) * p.c;
+      for (int kb = 0; kb < S::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) x = fmaxf(x, fmaxf(sacc[qb][kb][r], sacc[qb][kb][r + 1]));
+      mx[qb] = half_max(x) * p.c;
+    }
   };
 
   // One pipelined step for KV tile j.  On entry sc holds S^T of tile j and
@@ -232,50 +253,67 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
   // into sn on the MFMA pipe while the VALU turns tile j's scores into
   // probabilities and adds P_j V_j, and ends with the row maximum of tile
   // j+1, which overlaps the last PV products.  Tiles a wave does not need
-  // (past its diagonal, or past Nk) are fully masked, so the four waves run
-  // the same schedule.
-  float mnext;
+  // (past its diagonal, or past Nk) are fully masked, so all waves run the
+  // same schedule.
+  float mnext[NQB];
   auto step = [&](const lds_char* kr, const lds_char* vr, lds_char* kw, lds_char* vw,
-                  f32x16 (&sc)[S::KB], f32x16 (&sn)[S::KB], int j) {
+                  f32x16 (&sc)[NQB][S::KB], f32x16 (&sn)[NQB][S::KB], int j) {
     const int j0 = j * BN;
     if (needs_mask(j)) {
       mask_tile(sc, j);
-      mnext = tile_max(sc);
+      tile_max(sc, mnext);
     }
-    const float m_new = fmaxf(m_run, mnext);
-    if (__any(m_new > m_run + kRescaleThreshold)) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+    bool any_move = false;
+    float m_new[NQB];
 #pragma unroll
-      for (int db = 0; db < S::DB; ++db)
+    for (int qb = 0; qb < NQB; ++qb) {
+      m_new[qb] = fmaxf(m_run[qb], mnext[qb]);
+      any_move = any_move || (m_new[qb] > m_run[qb] + kRescaleThreshold);
+    }
+    if (__any(any_move)) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      m_run = m_new;
+      for (int qb = 0; qb < NQB; ++qb) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new[qb]);
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+        m_run[qb] = m_new[qb];
+      }
     }
     if (j + 2 < nkt) load_tile<D, BN, NW, false>(kbase, j0 + 2 * BN, p.Nk, kw, wave, lane);
     if (j + 1 < nkt) load_tile<D, BN, NW, true>(vbase, j0 + BN, p.Nk, vw, wave, lane);
 
-    // S^T of tile j+1 (its result is unused after the last tile).
-    s_tile(kr, sn);
+    // S^T of tile j+1 (its result is unused after the last tile).  With one
+    // 64-key block of 32 rows per wave it is issued first and overlaps tile
+    // j's softmax; with larger register tiles, computing it after the PV
+    // products keeps a single S^T tile live.
+    if constexpr (kPipe) s_tile(kr, sn);
 
     // Per 16-key chunk kc: probabilities P = 2^(S*c - m) become the bf16 B
     // operand (registers 8*(kc%2).. of block kc/2), then O^T += V^T P^T for
-    // every d block, the V^T operand coming from two transposing reads.  The
-    // row sum adds the fp32 probabilities: summing their bf16 roundings would
-    // put up to 2^-9 relative error into the LSE of short rows.
-    const float nm = -m_run;
-    float ls0 = 0.f, ls1 = 0.f;
+    // every d block, the V^T operand coming from two transposing reads and
+    // feeding NQB MFMAs.  The row sum adds the fp32 probabilities: summing
+    // their bf16 roundings would put up to 2^-9 relative error into the LSE
+    // of short rows.
 #pragma unroll
     for (int kc = 0; kc < S::KC; ++kc) {
-      bf16x8 pb;
+      bf16x8 pb[NQB];
 #pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[kc >> 1][8 * (kc & 1) + i], p.c, nm));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[kc >> 1][8 * (kc & 1) + i + 1], p.c, nm));
-        ls0 += e0;
-        ls1 += e1;
-        pb[i] = (__bf16)e0;
-        pb[i + 1] = (__bf16)e1;
+      for (int qb = 0; qb < NQB; ++qb) {
+        const float nm = -m_run[qb];
+        float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[qb][kc >> 1][8 * (kc & 1) + i], p.c, nm));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[qb][kc >> 1][8 * (kc & 1) + i + 1], p.c, nm));
+          ls0 += e0;
+          ls1 += e1;
+          pb[qb][i] = (__bf16)e0;
+          pb[qb][i + 1] = (__bf16)e1;
+        }
+        l_run[qb] += ls0 + ls1;
       }
 #pragma unroll
       for (int db = 0; db < S::DB; ++db) {
@@ -285,47 +323,58 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4*)(vr + dbo + 8 * S::RB));
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+          oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb], oacc[qb][db], 0, 0, 0);
       }
     }
-    l_run += ls0 + ls1;
 
-    mnext = tile_max(sn);
+    if constexpr (!kPipe) s_tile(kr, sn);
+    tile_max(sn, mnext);
     __syncthreads();
   };
 
   // Prologue: K_0, V_0, K_1 to LDS, S^T of tile 0 and its row maximum, then
   // a barrier so that the first step may overwrite K_0's buffer.
-  f32x16 sa[S::KB], sb[S::KB];
+  f32x16 sa[NQB][S::KB], sb[NQB][S::KB];   // sb unused without pipelining (see step)
   load_tile<D, BN, NW, false>(kbase, 0, p.Nk, kb0, wave, lane);
   load_tile<D, BN, NW, true>(vbase, 0, p.Nk, vb0, wave, lane);
   if (nkt > 1) load_tile<D, BN, NW, false>(kbase, BN, p.Nk, kb1, wave, lane);
   __syncthreads();
   s_tile(kb0, sa);
-  mnext = tile_max(sa);
+  tile_max(sa, mnext);
   __syncthreads();
   for (int j = 0; j < nkt; j += 2) {
-    step(kb1, vb0, kb0, vb1, sa, sb, j);
-    if (j + 1 < nkt) step(kb0, vb1, kb1, vb0, sb, sa, j + 1);
+    if constexpr (kPipe) {
+      step(kb1, vb0, kb0, vb1, sa, sb, j);
+      if (j + 1 < nkt) step(kb0, vb1, kb1, vb0, sb, sa, j + 1);
+    } else {
+      step(kb1, vb0, kb0, vb1, sa, sa, j);
+      if (j + 1 < nkt) step(kb0, vb1, kb1, vb0, sa, sa, j + 1);
+    }
   }
 
   // Epilogue: O = acc / l (bf16, round to nearest even), LSE in natural log.
-  const float l_tot = half_sum(l_run);
-  if (row < p.Nq) {
-    const float inv = 1.0f / l_tot;
-    uint16_t* orow = p.o + ((size_t)(b * p.Hq + h) * p.Nq + row) * D;
 #pragma unroll
-    for (int db = 0; db < S::DB; ++db)
+  for (int qb = 0; qb < NQB; ++qb) {
+    const float l_tot = half_sum(l_run[qb]);
+    if (row[qb] < p.Nq) {
+      const float inv = 1.0f / l_tot;
+      uint16_t* orow = p.o + ((size_t)(b * p.Hq + h) * p.Nq + row[qb]) * D;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        bf16x2 lo = {(__bf16)(oacc[db][4 * r4 + 0] * inv), (__bf16)(oacc[db][4 * r4 + 1] * inv)};
-        bf16x2 hi = {(__bf16)(oacc[db][4 * r4 + 2] * inv), (__bf16)(oacc[db][4 * r4 + 3] * inv)};
-        uint2 w;
-        w.x = __builtin_bit_cast(unsigned, lo);
-        w.y = __builtin_bit_cast(unsigned, hi);
-        *reinterpret_cast<uint2*>(orow + 32 * db + 8 * r4 + 4 * hl) = w;
-      }
-    if (hl == 0) p.lse[(size_t)(b * p.Hq + h) * p.Nq + row] = (m_run + log2f(l_tot)) * kLn2;
+      for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          bf16x2 lo = {(__bf16)(oacc[qb][db][4 * r4 + 0] * inv), (__bf16)(oacc[qb][db][4 * r4 + 1] * inv)};
+          bf16x2 hi = {(__bf16)(oacc[qb][db][4 * r4 + 2] * inv), (__bf16)(oacc[qb][db][4 * r4 + 3] * inv)};
+          uint2 w;
+          w.x = __builtin_bit_cast(unsigned, lo);
+          w.y = __builtin_bit_cast(unsigned, hi);
+          *reinterpret_cast<uint2*>(orow + 32 * db + 8 * r4 + 4 * hl) = w;
+        }
+      if (hl == 0)
+        p.lse[(size_t)(b * p.Hq + h) * p.Nq + row[qb]] = (m_run[qb] + log2f(l_tot)) * kLn2;
+    }
   }
 }
 
@@ -334,25 +383,28 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
 
 // Kernel symbols carry plain C names so that a profiler trace names exactly
 // which variant ran.
-#define FA_FWD_KERNEL(NAME, D, BN, NW, CAUSAL, WAVES_PER_EU)                          \
+#define FA_FWD_KERNEL(NAME, D, BN, NW, NQB, CAUSAL, WAVES_PER_EU)                    \
   extern "C" __global__ void __launch_bounds__(64 * NW, WAVES_PER_EU) NAME(           \
       fa::FwdParams p) {                                                              \
-    __shared__ __attribute__((aligned(1024))) char k0[fa::FwdShape<D, BN, NW>::TILE];    \
-    __shared__ __attribute__((aligned(1024))) char k1[fa::FwdShape<D, BN, NW>::TILE];    \
-    __shared__ __attribute__((aligned(1024))) char v0[fa::FwdShape<D, BN, NW>::TILE];    \
-    __shared__ __attribute__((aligned(1024))) char v1[fa::FwdShape<D, BN, NW>::TILE];    \
-    fa::fwd_body<D, BN, NW, CAUSAL>(p, (fa::lds_char*)k0, (fa::lds_char*)k1,             \
-                                    (fa::lds_char*)v0, (fa::lds_char*)v1);              \
+    using Sh = fa::FwdShape<D, BN, NW, NQB>;                                          \
+    __shared__ __attribute__((aligned(1024))) char k0[Sh::TILE];                      \
+    __shared__ __attribute__((aligned(1024))) char k1[Sh::TILE];                      \
+    __shared__ __attribute__((aligned(1024))) char v0[Sh::TILE];                      \
+    __shared__ __attribute__((aligned(1024))) char v1[Sh::TILE];                      \
+    fa::fwd_body<D, BN, NW, NQB, CAUSAL>(p, (fa::lds_char*)k0, (fa::lds_char*)k1,     \
+                                         (fa::lds_char*)v0, (fa::lds_char*)v1);       \
   }
 
-FA_FWD_KERNEL(fa_fwd_d32_nomask, 32, 64, 4, false, 2)
-FA_FWD_KERNEL(fa_fwd_d32_causal, 32, 64, 4, true, 2)
-FA_FWD_KERNEL(fa_fwd_d64_nomask, 64, 64, 4, false, 2)
-FA_FWD_KERNEL(fa_fwd_d64_causal, 64, 64, 4, true, 2)
-FA_FWD_KERNEL(fa_fwd_d128_nomask, 128, 64, 4, false, 2)
-FA_FWD_KERNEL(fa_fwd_d128_causal, 128, 64, 4, true, 2)
-FA_FWD_KERNEL(fa_fwd_d256_nomask, 256, 32, 4, false, 1)
-FA_FWD_KERNEL(fa_fwd_d256_causal, 256, 32, 4, true, 1)
+// Tile table (head dim: keys per tile, waves, query blocks of 32 rows per
+// wave, waves per SIMD).  It must match fwd_tile() below.
+FA_FWD_KERNEL(fa_fwd_d32_nomask, 32, 64, 4, 1, false, 2)
+FA_FWD_KERNEL(fa_fwd_d32_causal, 32, 64, 4, 1, true, 2)
+FA_FWD_KERNEL(fa_fwd_d64_nomask, 64, 64, 4, 1, false, 2)
+FA_FWD_KERNEL(fa_fwd_d64_causal, 64, 64, 4, 1, true, 2)
+FA_FWD_KERNEL(fa_fwd_d128_nomask, 128, 64, 8, 1, false, 2)
+FA_FWD_KERNEL(fa_fwd_d128_causal, 128, 64, 8, 1, true, 2)
+FA_FWD_KERNEL(fa_fwd_d256_nomask, 256, 32, 4, 1, false, 1)
+FA_FWD_KERNEL(fa_fwd_d256_causal, 256, 32, 4, 1, true, 1)
 
 namespace fa {
 
@@ -360,7 +412,7 @@ FwdTile fwd_tile(int d) {
   switch (d) {
     case 32: return {128, 64, 4};
     case 64: return {128, 64, 4};
-    case 128: return {128, 64, 4};
+    case 128: return {256, 64, 8};
     case 256: return {128, 32, 4};
     default: return {0, 0, 0};
   }
