@@ -110,7 +110,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)   # ~50 ms: the clocks ramp up first
     ap.add_argument("--splits", type=int, default=0, help="decode splits (0 = heuristic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -213,7 +213,7 @@ def main():
             "workload": "causal prefill B=1 H=32 N=16384 d=128 + split-KV decode B=8 Hq=32 "
                         "Hkv=8 Nk=32768 d=128",
             "fwd": {"B": fcfg.B, "H": fcfg.Hq, "N": fcfg.Nq, "d": fcfg.d, "causal": True,
-                    "scale": fcfg.scale, "kernel": fa.fa_fwd_kernel_name(fcfg.d, 1),
+                    "scale": fcfg.scale, "kernel": fa.fa_fwd_kernel_name(fcfg.d, 1, fcfg.Nq, fcfg.Nk),
                     "flop": flop, "ms": round(f_ms, 5), "ms_min": round(min(fwd_ms), 5)},
             "decode": {"B": dcfg.B, "Hq": dcfg.Hq, "Hkv": dcfg.Hkv, "Nk": dcfg.Nk, "d": dcfg.d,
                        "splits": S,
@@ -227,7 +227,7 @@ def main():
             "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": _traffic("fa_fwd_d128_causal", srcs),
-            "kernel": fa.fa_fwd_kernel_name(fcfg.d, 1),
+            "kernel": fa.fa_fwd_kernel_name(fcfg.d, 1, fcfg.Nq, fcfg.Nk),
             "algorithmic_bytes": fwd_bytes,
         },
         "decode": {

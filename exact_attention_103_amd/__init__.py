@@ -41,7 +41,7 @@ _SIGNATURES = {
     "fa_decode_max_splits": (_i, [_i]),
     "fa_strerror": (_cs, [_i]),
     "fa_last_hip_error": (_cs, []),
-    "fa_fwd_kernel_name": (_cs, [_i, _i]),
+    "fa_fwd_kernel_name": (_cs, [_i, _i, _i, _i]),
     "fa_decode_kernel_name": (_cs, [_i, _i, _i]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
@@ -111,8 +111,8 @@ def fa_last_hip_error():
     return lib().fa_last_hip_error().decode()
 
 
-def fa_fwd_kernel_name(d, causal):
-    r = lib().fa_fwd_kernel_name(d, int(causal))
+def fa_fwd_kernel_name(d, causal, Nq, Nk):
+    r = lib().fa_fwd_kernel_name(d, int(causal), Nq, Nk)
     return r.decode() if r else None
 
 

@@ -76,7 +76,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   const int64_t q_bytes = checked_product({B, Hq, Nq, d, 2});
   const int64_t kv_bytes = checked_product({B, Hkv, Nk, d, 2});
   const int64_t lse_bytes = checked_product({B, Hq, Nq, 4});
-  const fa::FwdTile t = fa::fwd_tile(d);
+  const fa::FwdTile t = fa::fwd_tile(d, causal != 0, Nq, Nk);
   const int64_t grid = checked_product({(Nq + t.bm - 1) / t.bm, B, Hq});
   if (q_bytes < 0 || kv_bytes < 0 || lse_bytes < 0 || grid < 0 || grid > INT32_MAX)
     return FA_ERR_TOO_LARGE;
@@ -200,9 +200,10 @@ const char* fa_strerror(int status) {
 
 const char* fa_last_hip_error(void) { return g_hip_error; }
 
-const char* fa_fwd_kernel_name(int d, int causal) {
+const char* fa_fwd_kernel_name(int d, int causal, int Nq, int Nk) {
   if (causal != 0 && causal != 1) return nullptr;
-  return fa::fwd_kernel_name(d, causal != 0);
+  if (Nq <= 0 || Nk <= 0) return nullptr;
+  return fa::fwd_kernel_name(d, causal != 0, Nq, Nk);
 }
 
 const char* fa_decode_kernel_name(int d, int hq_per_kv, int stage) {

@@ -70,9 +70,10 @@ struct FwdShape {
   static constexpr int CPR = D / 8;       // 16-byte chunks per row
   static constexpr int TILE = BN * RB;    // bytes of one K (or V) tile
   static constexpr int CHUNKS = BN * CPR;
-  static constexpr int LOADS = CHUNKS / (64 * NW);   // 1 KB wave loads per tile per wave
+  static constexpr int BLKS = CHUNKS / 64;              // 1 KB blocks per tile
+  static constexpr int LOADS = (BLKS + NW - 1) / NW;    // wave loads per tile per wave
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
-  static_assert(CHUNKS % (64 * NW) == 0, "whole wave loads");
+  static_assert(CHUNKS % 64 == 0, "whole 1 KB blocks");
 };
 
 // LDS layouts (16-byte chunk c of row r is stored at chunk c ^ X(r)):
@@ -105,7 +106,8 @@ __device__ __forceinline__ float half_sum(float x) {
 }
 
 // Issue the wave's share of one K or V tile as direct global -> LDS loads.
-// Wave load i writes 1 KB block (i*NW + wave) of the tile; lane l of that
+// Wave load i writes 1 KB block (i*NW + wave) of the tile (when the tile has
+// fewer blocks than waves, only the first waves load); lane l of that
 // load fetches the global chunk whose swizzled position is that block's l-th
 // chunk.  Rows past Nk re-read row Nk-1 (finite data; those keys are masked).
 template <int D, int BN, int NW, bool IS_V>
@@ -114,7 +116,8 @@ __device__ __forceinline__ void load_tile(const uint16_t* base, int j0, int Nk, 
   using S = FwdShape<D, BN, NW, 1>;
 #pragma unroll
   for (int i = 0; i < S::LOADS; ++i) {
-    const int blk = i * NW + wave;
+    const int blk = i * NW + wave;   // uniform across the wave
+    if (S::BLKS % NW != 0 && blk >= S::BLKS) break;
     const int P = blk * 64 + lane;
     const int row = P / S::CPR;
     const int pc = P % S::CPR;
@@ -396,40 +399,60 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
   }
 
 // Tile table (head dim: keys per tile, waves, query blocks of 32 rows per
-// wave, waves per SIMD).  It must match fwd_tile() below.
-FA_FWD_KERNEL(fa_fwd_d32_nomask, 32, 64, 4, 1, false, 2)
-FA_FWD_KERNEL(fa_fwd_d32_causal, 32, 64, 4, 1, true, 2)
+// wave, waves per SIMD).  It must match fwd_tile() below.  d = 128 has a
+// 256-row tile (8 waves share each K/V tile, for long key ranges) and a
+// 128-row tile (more workgroups per CU, for short ones).
+FA_FWD_KERNEL(fa_fwd_d32_nomask, 32, 128, 4, 1, false, 2)
+FA_FWD_KERNEL(fa_fwd_d32_causal, 32, 128, 4, 1, true, 2)
 FA_FWD_KERNEL(fa_fwd_d64_nomask, 64, 64, 4, 1, false, 2)
 FA_FWD_KERNEL(fa_fwd_d64_causal, 64, 64, 4, 1, true, 2)
 FA_FWD_KERNEL(fa_fwd_d128_nomask, 128, 64, 8, 1, false, 2)
 FA_FWD_KERNEL(fa_fwd_d128_causal, 128, 64, 8, 1, true, 2)
+FA_FWD_KERNEL(fa_fwd_d128_nomask_bm128, 128, 64, 4, 1, false, 2)
+FA_FWD_KERNEL(fa_fwd_d128_causal_bm128, 128, 64, 4, 1, true, 2)
 FA_FWD_KERNEL(fa_fwd_d256_nomask, 256, 32, 4, 1, false, 1)
 FA_FWD_KERNEL(fa_fwd_d256_causal, 256, 32, 4, 1, true, 1)
 
 namespace fa {
+namespace {
 
-FwdTile fwd_tile(int d) {
+// Which compiled variant runs: 0 = the head dim's default tile, 1 = the
+// 128-row d = 128 tile, chosen when a workgroup would see few key tiles
+// (about Nk/128 on average when causal, Nk/64 otherwise).
+int fwd_variant(int d, bool causal, int Nk) {
+  if (d != 128) return 0;
+  return (causal ? Nk < 4096 : Nk < 2048) ? 1 : 0;
+}
+
+}  // namespace
+
+FwdTile fwd_tile(int d, bool causal, int Nq, int Nk) {
+  (void)Nq;
   switch (d) {
-    case 32: return {128, 64, 4};
+    case 32: return {128, 128, 4};
     case 64: return {128, 64, 4};
-    case 128: return {256, 64, 8};
+    case 128: return fwd_variant(d, causal, Nk) ? FwdTile{128, 64, 4} : FwdTile{256, 64, 8};
     case 256: return {128, 32, 4};
     default: return {0, 0, 0};
   }
 }
 
-const char* fwd_kernel_name(int d, bool causal) {
+const char* fwd_kernel_name(int d, bool causal, int Nq, int Nk) {
+  (void)Nq;
   switch (d) {
     case 32: return causal ? "fa_fwd_d32_causal" : "fa_fwd_d32_nomask";
     case 64: return causal ? "fa_fwd_d64_causal" : "fa_fwd_d64_nomask";
-    case 128: return causal ? "fa_fwd_d128_causal" : "fa_fwd_d128_nomask";
+    case 128:
+      if (fwd_variant(d, causal, Nk))
+        return causal ? "fa_fwd_d128_causal_bm128" : "fa_fwd_d128_nomask_bm128";
+      return causal ? "fa_fwd_d128_causal" : "fa_fwd_d128_nomask";
     case 256: return causal ? "fa_fwd_d256_causal" : "fa_fwd_d256_nomask";
     default: return nullptr;
   }
 }
 
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t s) {
-  const FwdTile t = fwd_tile(d);
+  const FwdTile t = fwd_tile(d, causal, p.Nq, p.Nk);
   const int nqb = (p.Nq + t.bm - 1) / t.bm;
   const dim3 grid((unsigned)(nqb * p.B * p.Hq));
   const dim3 block((unsigned)(64 * t.waves));
@@ -437,7 +460,12 @@ hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t s) {
   switch (d) {
     case 32: fn = causal ? (const void*)fa_fwd_d32_causal : (const void*)fa_fwd_d32_nomask; break;
     case 64: fn = causal ? (const void*)fa_fwd_d64_causal : (const void*)fa_fwd_d64_nomask; break;
-    case 128: fn = causal ? (const void*)fa_fwd_d128_causal : (const void*)fa_fwd_d128_nomask; break;
+    case 128:
+      if (fwd_variant(d, causal, p.Nk))
+        fn = causal ? (const void*)fa_fwd_d128_causal_bm128 : (const void*)fa_fwd_d128_nomask_bm128;
+      else
+        fn = causal ? (const void*)fa_fwd_d128_causal : (const void*)fa_fwd_d128_nomask;
+      break;
     case 256: fn = causal ? (const void*)fa_fwd_d256_causal : (const void*)fa_fwd_d256_nomask; break;
     default: return hipErrorInvalidValue;
   }

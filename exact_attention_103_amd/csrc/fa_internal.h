@@ -49,12 +49,13 @@ struct DecodeParams {
 // arguments were validated and return the hipError_t of the launch.
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t s);
-const char* fwd_kernel_name(int d, bool causal);
+const char* fwd_kernel_name(int d, bool causal, int Nq, int Nk);
 const char* decode_kernel_name(int d, int group, int stage);
 
-// Tile shape of the forward kernel for head dimension d (BM = 32 * waves).
+// Tile shape of the forward kernel that runs for a problem (BM query rows
+// per workgroup, BN keys per tile, waves per workgroup).
 struct FwdTile { int bm, bn, waves; };
-FwdTile fwd_tile(int d);
+FwdTile fwd_tile(int d, bool causal, int Nq, int Nk);
 
 // Query heads handled by one decode split workgroup: the largest of 16, 8,
 // 4, 2, 1 that divides the number of query heads per KV head.

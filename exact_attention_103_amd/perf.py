@@ -1,0 +1,99 @@
+"""Throughput table for every workload shape (one GPU).
+
+    python -m exact_attention_103_amd.perf [--iters 20] [--warmup 5]
+
+Prints one JSON line per workload: the kernel that ran, the median launch
+time (HIP events on the launch stream) and TFLOP/s for the forward (flop =
+4*B*H*Nq*Nk*d, halved when causal) or GB/s for the decode (K + V cache read
+once, plus q, O and LSE).  Inputs are random bf16 tensors of the workload's
+shape and scaling; the forward's speed does not depend on the values.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+
+import torch
+
+import exact_attention_103_amd as fa
+
+FWD = [  # name, B, H, N, d, causal, input scale
+    ("train_nc", 8, 16, 2048, 128, False, 1.0),
+    ("train_c", 8, 16, 2048, 128, True, 1.0),
+    ("long", 1, 32, 16384, 128, True, 1.0),
+    ("sweep_d32", 2, 16, 4096, 32, True, 32 ** -0.5),
+    ("sweep_d64", 2, 16, 4096, 64, True, 64 ** -0.5),
+    ("sweep_d128", 2, 16, 4096, 128, True, 128 ** -0.5),
+    ("sweep_d256", 2, 16, 4096, 256, True, 256 ** -0.5),
+]
+DECODE = [(8, 32, 8, 32768, 128, s) for s in (0, 16, 32, 64)]
+
+
+def _time(fn, iters, warmup):
+    st = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(iters):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        fn()
+        b.record(st)
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(x.elapsed_time(y) for x, y in ev)
+    return ms[len(ms) // 2]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--iters", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    args = ap.parse_args()
+    torch.manual_seed(0)
+    # Bring the clocks up before the first measurement: they ramp over the
+    # first ~50 ms of sustained work (this is ~150 ms).
+    q = torch.randn(1, 32, 8192, 128, device="cuda").to(torch.bfloat16)
+    for _ in range(300):
+        fa.fwd(q, q, q, causal=True)
+    torch.cuda.synchronize()
+    del q
+    for name, B, H, N, d, causal, sc in FWD:
+        q = (torch.randn(B, H, N, d, device="cuda") * sc).to(torch.bfloat16)
+        k = (torch.randn(B, H, N, d, device="cuda") * sc).to(torch.bfloat16)
+        v = torch.randn(B, H, N, d, device="cuda").to(torch.bfloat16)
+        o = torch.empty_like(q)
+        lse = torch.empty(B, H, N, device="cuda", dtype=torch.float32)
+        ms = _time(lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse), args.iters, args.warmup)
+        flop = 4.0 * B * H * N * N * d / (2 if causal else 1)
+        print(json.dumps({"workload": name, "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                          "kernel": fa.fa_fwd_kernel_name(d, int(causal), N, N), "ms": round(ms, 4),
+                          "tflops": round(flop / ms / 1e9, 1),
+                          "pct_of_2500": round(100 * flop / ms / 1e9 / 2500, 1)}), flush=True)
+        del q, k, v, o, lse
+    for B, Hq, Hkv, Nk, d, S in DECODE:
+        q = torch.randn(B, Hq, d, device="cuda").to(torch.bfloat16)
+        kc = torch.randn(B, Hkv, Nk, d, device="cuda").to(torch.bfloat16)
+        vc = torch.randn(B, Hkv, Nk, d, device="cuda").to(torch.bfloat16)
+        splits = S or fa.fa_decode_num_splits(B, Hq, Hkv, Nk, d)
+        ws = torch.empty(fa.fa_decode_workspace_size(B, Hq, d, splits), dtype=torch.uint8,
+                         device="cuda")
+        o = torch.empty_like(q)
+        lse = torch.empty(B, Hq, device="cuda", dtype=torch.float32)
+        ms = _time(lambda: fa.decode(q, kc, vc, num_splits=splits, out=o, lse=lse, workspace=ws),
+                   args.iters, args.warmup)
+        nbytes = 2 * B * Hkv * Nk * d * 2 + 2 * B * Hq * d * 2 + 4 * B * Hq
+        print(json.dumps({"workload": "decode", "B": B, "Hq": Hq, "Hkv": Hkv, "Nk": Nk, "d": d,
+                          "splits": splits, "kernels": [fa.fa_decode_kernel_name(d, Hq // Hkv, 0),
+                                                        fa.fa_decode_kernel_name(d, Hq // Hkv, 1)],
+                          "ms": round(ms, 4), "gbs": round(nbytes / ms / 1e6, 1),
+                          "pct_of_8000": round(100 * nbytes / ms / 1e6 / 8000, 1)}), flush=True)
+        del q, kc, vc, ws, o, lse
+
+
+if __name__ == "__main__":
+    main()

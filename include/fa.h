@@ -127,10 +127,12 @@ const char* fa_strerror(int status);
 const char* fa_last_hip_error(void);
 
 /* Kernel symbol names, as a profiler reports them, so a benchmark can
- * confirm which kernel ran.  NULL for an unsupported head dimension.
+ * confirm which kernel ran.  NULL for an unsupported head dimension or
+ * invalid sizes.  fa_fwd_kernel_name: the forward kernel fa_fwd launches for
+ * these sizes (the tile depends on d and, for d = 128, on the key length).
  * fa_decode_kernel_name: stage 0 = split kernel (depends on the number of
  * query heads per KV head), stage 1 = merge kernel. */
-const char* fa_fwd_kernel_name(int d, int causal);
+const char* fa_fwd_kernel_name(int d, int causal, int Nq, int Nk);
 const char* fa_decode_kernel_name(int d, int hq_per_kv, int stage);
 
 #ifdef __cplusplus

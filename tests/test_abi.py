@@ -62,16 +62,22 @@ def test_status_enum_matches_header():
 
 def test_kernel_names():
     for d in (32, 64, 128, 256):
-        assert fa.fa_fwd_kernel_name(d, 0) == f"fa_fwd_d{d}_nomask"
-        assert fa.fa_fwd_kernel_name(d, 1) == f"fa_fwd_d{d}_causal"
+        assert fa.fa_fwd_kernel_name(d, 0, 16384, 16384) == f"fa_fwd_d{d}_nomask"
+        assert fa.fa_fwd_kernel_name(d, 1, 16384, 16384) == f"fa_fwd_d{d}_causal"
         assert fa.fa_decode_kernel_name(d, 4, 0) == f"fa_decode_split_d{d}_g4"
         assert fa.fa_decode_kernel_name(d, 6, 0) == f"fa_decode_split_d{d}_g2"
         assert fa.fa_decode_kernel_name(d, 3, 0) == f"fa_decode_split_d{d}_g1"
         assert fa.fa_decode_kernel_name(d, 16, 0) == f"fa_decode_split_d{d}_g16"
         assert fa.fa_decode_kernel_name(d, 24, 0) == f"fa_decode_split_d{d}_g8"
         assert fa.fa_decode_kernel_name(d, 4, 1) == f"fa_decode_merge_d{d}"
-    assert fa.fa_fwd_kernel_name(96, 0) is None
-    assert fa.fa_fwd_kernel_name(128, 2) is None
+    # d = 128 switches to the 128-row tile for short key ranges.
+    assert fa.fa_fwd_kernel_name(128, 1, 2048, 2048) == "fa_fwd_d128_causal_bm128"
+    assert fa.fa_fwd_kernel_name(128, 1, 4096, 4096) == "fa_fwd_d128_causal"
+    assert fa.fa_fwd_kernel_name(128, 0, 1024, 1024) == "fa_fwd_d128_nomask_bm128"
+    assert fa.fa_fwd_kernel_name(128, 0, 2048, 2048) == "fa_fwd_d128_nomask"
+    assert fa.fa_fwd_kernel_name(96, 0, 64, 64) is None
+    assert fa.fa_fwd_kernel_name(128, 2, 64, 64) is None
+    assert fa.fa_fwd_kernel_name(128, 0, 0, 64) is None
     assert fa.fa_decode_kernel_name(128, 4, 2) is None
     assert fa.fa_decode_kernel_name(48, 4, 0) is None
 
