@@ -110,7 +110,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=20)   # ~50 ms: the clocks ramp up first
+    ap.add_argument("--warmup", type=int, default=30)   # ~70 ms: the clocks ramp up first
     ap.add_argument("--splits", type=int, default=0, help="decode splits (0 = heuristic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
