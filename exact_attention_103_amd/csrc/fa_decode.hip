@@ -241,15 +241,20 @@ __device__ __forceinline__ void decode_split_body(const DecodeParams& p, lds_cha
   }
 }
 
-// Merge: one workgroup of kMergeThreads per (b, query head).  The split
-// LSEs are read in parallel and reduced through LDS; then thread t sums the
-// splits s = t / D, t / D + SP, ... for output column t % D with independent
-// loads, and the SP partial sums per column are added in a fixed order.
+// Merge: one workgroup of kMergeThreads per (b, query head).  Thread t owns
+// output column t % D and the splits s = t / D, t / D + SP, ...; it loads
+// their LSEs and partial outputs in batches of kMergeBatch independent
+// loads.  The first batch is issued before the maximum LSE is known: every
+// wave finds that maximum itself (strided loads and a shuffle reduction), so
+// the partial outputs cost no second round trip.  The SP partial sums per
+// column are then added through LDS in a fixed order.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeBatch = 8;
 
 template <int D>
 __device__ __forceinline__ void decode_merge_body(const DecodeParams& p) {
   constexpr int SP = kMergeThreads / D;       // split phases per column
+  constexpr int U = kMergeBatch;
   __shared__ float red[kMergeThreads];
   __shared__ float part[kMergeThreads];
   const int tid = threadIdx.x;
@@ -257,26 +262,36 @@ __device__ __forceinline__ void decode_merge_body(const DecodeParams& p) {
   const int S = p.splits;
   const float* lp = p.lse_part + (size_t)bh * S;
   const float* op = p.o_part + (size_t)bh * S * D;
-
-  float mx = -INFINITY;
-  for (int s = tid; s < S; s += kMergeThreads) mx = max_raw(mx, lp[s]);
-  red[tid] = mx;
-  __syncthreads();
-  for (int w = kMergeThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] = max_raw(red[tid], red[tid + w]);
-    __syncthreads();
-  }
-  const float M = red[0];   // finite: chunk 0 always holds at least one key
-  __syncthreads();
-
   const int dd = tid % D, ph = tid / D;
+
+  float ls[U], ov[U];
+  auto load_batch = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * SP;
+      ls[u] = s < S ? lp[s] : -INFINITY;
+      ov[u] = s < S ? op[(size_t)s * D + dd] : 0.f;
+    }
+  };
+  load_batch(ph);
+
+  float M = -INFINITY;
+  for (int s = tid & 63; s < S; s += 64) M = max_raw(M, lp[s]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = max_raw(M, __shfl_xor(M, off));
+  // M is finite: chunk 0 always holds at least one key.
+
   float O = 0.f, W = 0.f;
-#pragma unroll 8
-  for (int s = ph; s < S; s += SP) {
-    const float ls = lp[s];
-    const float w = ls == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ls - M) * kLog2e);
-    W += w;
-    O += w * op[(size_t)s * D + dd];
+  for (int s0 = ph;;) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = ls[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ls[u] - M) * kLog2e);
+      W += w;
+      O += w * ov[u];
+    }
+    s0 += U * SP;
+    if (s0 >= S) break;
+    load_batch(s0);
   }
   part[tid] = O;
   red[tid] = W;

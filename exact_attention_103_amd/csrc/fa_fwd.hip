@@ -191,13 +191,13 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
   const int voff = vrow * S::RB + 32 * ((lane >> 4) & 1) + 16 * ((j16 & 3) >> 1) + 8 * (j16 & 1);
 
   f32x16 oacc[NQB][S::DB];
-  float m_run[NQB], l_run[NQB];
+  float m_run[NQB], l_run[NQB][2];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
 #pragma unroll
     for (int db = 0; db < S::DB; ++db) oacc[qb][db] = f32x16{};
     m_run[qb] = -1e30f;   // finite, so 2^(m_old - m_new) is never inf - inf
-    l_run[qb] = 0.f;      // partial row sum over this lane half's keys
+    l_run[qb][0] = l_run[qb][1] = 0.f;   // partial row sums over this lane half's keys
   }
 
   // S^T = K Q^T for one tile; every K operand read from LDS feeds NQB MFMAs.
@@ -243,7 +243,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
 #pragma unroll
       for (int kb = 0; kb < S::KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) x = fmaxf(x, fmaxf(sacc[qb][kb][r], sacc[qb][kb][r + 1]));
+        for (int r = 0; r < 16; r += 2) x = fmaxf(fmaxf(x, sacc[qb][kb][r]), sacc[qb][kb][r + 1]);   // v_max3 chain
       mx[qb] = half_max(x) * p.c;
     }
   };
@@ -277,7 +277,8 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new[qb]);
-        l_run[qb] *= alpha;
+        l_run[qb][0] *= alpha;
+        l_run[qb][1] *= alpha;
 #pragma unroll
         for (int db = 0; db < S::DB; ++db)
 #pragma unroll
@@ -306,17 +307,15 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         const float nm = -m_run[qb];
-        float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
           const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[qb][kc >> 1][8 * (kc & 1) + i], p.c, nm));
           const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[qb][kc >> 1][8 * (kc & 1) + i + 1], p.c, nm));
-          ls0 += e0;
-          ls1 += e1;
+          l_run[qb][0] += e0;   // two running sums: one add per probability
+          l_run[qb][1] += e1;
           pb[qb][i] = (__bf16)e0;
           pb[qb][i + 1] = (__bf16)e1;
         }
-        l_run[qb] += ls0 + ls1;
       }
 #pragma unroll
       for (int db = 0; db < S::DB; ++db) {
@@ -360,7 +359,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
   // Epilogue: O = acc / l (bf16, round to nearest even), LSE in natural log.
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
-    const float l_tot = half_sum(l_run[qb]);
+    const float l_tot = half_sum(l_run[qb][0] + l_run[qb][1]);
     if (row[qb] < p.Nq) {
       const float inv = 1.0f / l_tot;
       uint16_t* orow = p.o + ((size_t)(b * p.Hq + h) * p.Nq + row[qb]) * D;

@@ -13,7 +13,7 @@ from __future__ import annotations
 
 import argparse
 import json
-import math
+import time
 
 import torch
 
@@ -31,11 +31,18 @@ FWD = [  # name, B, H, N, d, causal, input scale
 DECODE = [(8, 32, 8, 32768, 128, s) for s in (0, 16, 32, 64)]
 
 
-def _time(fn, iters, warmup):
+def _time(fn, iters, warmup, warm_ms=200.0):
+    """Median launch time after `warmup` launches and at least `warm_ms` of
+    back-to-back launches of the same call (the clocks settle only after
+    ~50 ms of sustained work)."""
     st = torch.cuda.current_stream()
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or (time.perf_counter() - t0) * 1e3 < warm_ms:
+        for _ in range(max(warmup, 1)):
+            fn()
+        n += max(warmup, 1)
+        torch.cuda.synchronize()
     ev = []
     for _ in range(iters):
         a = torch.cuda.Event(enable_timing=True)
@@ -55,13 +62,6 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     args = ap.parse_args()
     torch.manual_seed(0)
-    # Bring the clocks up before the first measurement: they ramp over the
-    # first ~50 ms of sustained work (this is ~150 ms).
-    q = torch.randn(1, 32, 8192, 128, device="cuda").to(torch.bfloat16)
-    for _ in range(300):
-        fa.fwd(q, q, q, causal=True)
-    torch.cuda.synchronize()
-    del q
     for name, B, H, N, d, causal, sc in FWD:
         q = (torch.randn(B, H, N, d, device="cuda") * sc).to(torch.bfloat16)
         k = (torch.randn(B, H, N, d, device="cuda") * sc).to(torch.bfloat16)
