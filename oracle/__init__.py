@@ -2,12 +2,15 @@
 
 Only ``tests/``, the smoke check and the benchmark's CPU-baseline leg may
 import this package.  It shares no code with the HIP library.  See
-``oracle/attention.py`` for what each function computes and which passage of
-the pages it follows.
+``oracle/attention.py`` (forward, decode) and ``oracle/attention_bwd.py``
+(gradients) for what each function computes and which passage of the pages
+it follows.
 """
 
 from .attention import (allowed_keys, attention_head_ref, attention_ref,
                         merge_partials, merge_ref, online_ref)
+from .attention_bwd import attention_bwd_head_ref, attention_bwd_ref
 
 __all__ = ["allowed_keys", "attention_head_ref", "attention_ref",
-           "merge_partials", "merge_ref", "online_ref"]
+           "merge_partials", "merge_ref", "online_ref",
+           "attention_bwd_head_ref", "attention_bwd_ref"]
