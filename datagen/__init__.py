@@ -6,7 +6,9 @@ parity test consume the exact same bit patterns.
 
 Recipe (the pages name no dataset; every workload is synthetic):
   * ``numpy.random.default_rng(seed)`` (PCG64);
-  * ``standard_normal(shape, dtype=float32)`` drawn in the order q, k, v;
+  * ``standard_normal(shape, dtype=float32)`` drawn in the order q, k, v
+    (and, for the backward pass, the output gradient dO after them, so q, k
+    and v equal the forward inputs of the same workload);
   * optionally multiplied by ``input_scale`` in float32 (the head-dim sweep
     scales by 1/sqrt(d) before rounding);
   * rounded to bfloat16 by round-to-nearest-even on the float32 bit pattern.
@@ -33,6 +35,7 @@ __all__ = [
     "decode_config",
     "make_fwd_inputs",
     "make_decode_inputs",
+    "make_bwd_inputs",
     "row_subset",
 ]
 
@@ -139,6 +142,15 @@ def make_fwd_inputs(cfg: AttnConfig):
         cfg.seed,
         [(cfg.B, cfg.Hq, cfg.Nq, cfg.d), (cfg.B, cfg.Hkv, cfg.Nk, cfg.d),
          (cfg.B, cfg.Hkv, cfg.Nk, cfg.d)],
+        cfg.input_scale)
+
+
+def make_bwd_inputs(cfg: AttnConfig):
+    """bf16 bits for q, k, v (as make_fwd_inputs) and dO [B][Hq][Nq][d]."""
+    return gaussian_bf16(
+        cfg.seed,
+        [(cfg.B, cfg.Hq, cfg.Nq, cfg.d), (cfg.B, cfg.Hkv, cfg.Nk, cfg.d),
+         (cfg.B, cfg.Hkv, cfg.Nk, cfg.d), (cfg.B, cfg.Hq, cfg.Nq, cfg.d)],
         cfg.input_scale)
 
 

@@ -18,7 +18,8 @@ __all__ = [
     "FAError", "lib", "fa_fwd", "fa_decode_splitkv", "fa_decode_workspace_size",
     "fa_decode_num_splits", "fa_decode_max_splits", "fa_strerror",
     "fa_last_hip_error", "fa_fwd_kernel_name", "fa_decode_kernel_name",
-    "fwd", "decode", "EXPORTED_SYMBOLS", "LIB_PATH",
+    "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_kernel_name",
+    "fwd", "decode", "bwd", "EXPORTED_SYMBOLS", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -43,6 +44,10 @@ _SIGNATURES = {
     "fa_last_hip_error": (_cs, []),
     "fa_fwd_kernel_name": (_cs, [_i, _i, _i, _i]),
     "fa_decode_kernel_name": (_cs, [_i, _i, _i]),
+    "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
+                    _i, _vp, _sz, _vp]),
+    "fa_bwd_workspace_size": (_sz, [_i, _i, _i]),
+    "fa_bwd_kernel_name": (_cs, [_i, _i, _i]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -89,6 +94,21 @@ def fa_decode_splitkv(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nk, d, scale,
     return lib().fa_decode_splitkv(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nk, d,
                                    scale, num_splits, workspace, workspace_bytes,
                                    stream)
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+           workspace, workspace_bytes, stream=None):
+    return lib().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale,
+                        int(causal), workspace, workspace_bytes, stream)
+
+
+def fa_bwd_workspace_size(B, Hq, Nq):
+    return lib().fa_bwd_workspace_size(B, Hq, Nq)
+
+
+def fa_bwd_kernel_name(d, causal, stage):
+    r = lib().fa_bwd_kernel_name(d, int(causal), stage)
+    return r.decode() if r else None
 
 
 def fa_decode_workspace_size(B, Hq, d, num_splits):
@@ -195,3 +215,34 @@ def decode(q, k_cache, v_cache, scale=None, num_splits=0, out=None, lse=None,
     if rc != FA_OK:
         raise FAError(rc, "fa_decode_splitkv")
     return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, causal=False, scale=None, workspace=None):
+    """dQ, dK, dV of attention; q/o/dout [B][Hq][Nq][d], k/v [B][Hkv][Nk][d] bf16,
+    lse [B][Hq][Nq] fp32 (the forward's outputs o and lse)."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_bf16(name, t, 4)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B][Hkv][Nk][d] with q's B and d")
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("o and dout must have q's shape")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B][Hq][Nq] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    need = fa_bwd_workspace_size(B, Hq, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq,
+                Nk, d, float(scale), int(bool(causal)), workspace.data_ptr(), workspace.numel(),
+                _stream_ptr())
+    if rc != FA_OK:
+        raise FAError(rc, "fa_bwd")
+    return dq, dk, dv

@@ -181,14 +181,81 @@ int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache, v
   return e == hipSuccess ? FA_OK : hip_fail(e);
 }
 
+size_t fa_bwd_workspace_size(int B, int Hq, int Nq) {
+  const int64_t n = checked_product({B, Hq, Nq, 4});
+  return n < 0 ? 0 : static_cast<size_t>(n);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
+           int Nk, int d, float scale, int causal, void* workspace, size_t workspace_bytes,
+           void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (causal && Nq > Nk) return FA_ERR_SHAPE;
+  if (!fa::bwd_supported_d(d)) return FA_ERR_HEAD_DIM;
+  if (!scale_ok(scale)) return FA_ERR_SCALE;
+  const size_t need = fa_bwd_workspace_size(B, Hq, Nq);
+  if (need == 0) return FA_ERR_TOO_LARGE;
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      !aligned16(workspace))
+    return FA_ERR_ALIGN;
+
+  const int64_t q_bytes = checked_product({B, Hq, Nq, d, 2});
+  const int64_t kv_bytes = checked_product({B, Hkv, Nk, d, 2});
+  const int64_t lse_bytes = checked_product({B, Hq, Nq, 4});
+  const int64_t g1 = checked_product({(Nq + 127) / 128, B, Hq});
+  const int64_t g2 = checked_product({(Nk + 127) / 128, B, Hkv});
+  if (q_bytes < 0 || kv_bytes < 0 || lse_bytes < 0 || g1 < 0 || g1 > INT32_MAX || g2 < 0 ||
+      g2 > INT32_MAX)
+    return FA_ERR_TOO_LARGE;
+
+  const Span ins[6] = {span(q, q_bytes), span(k, kv_bytes), span(v, kv_bytes),
+                       span(o, q_bytes), span(dout, q_bytes), span(lse, lse_bytes)};
+  const Span outs[4] = {span(dq, q_bytes), span(dk, kv_bytes), span(dv, kv_bytes),
+                        span(workspace, static_cast<int64_t>(need))};
+  for (int i = 0; i < 4; ++i) {
+    for (const Span& in : ins)
+      if (overlaps(outs[i], in)) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outs[j])) return FA_ERR_ALIAS;
+  }
+
+  fa::BwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(o);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.delta = static_cast<float*>(workspace);
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.group = Hq / Hkv;
+  p.c = scale * fa::kLog2e;
+  p.scale = scale;
+  const hipError_t e = fa::launch_bwd(p, d, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : hip_fail(e);
+}
+
 const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "success";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid shape (sizes must be > 0, Hq a multiple of Hkv, causal needs Nq <= Nk)";
-    case FA_ERR_HEAD_DIM: return "unsupported head dimension (32, 64, 128 or 256)";
+    case FA_ERR_HEAD_DIM: return "unsupported head dimension (32, 64, 128 or 256; backward: 32, 64 or 128)";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
-    case FA_ERR_WORKSPACE: return "decode workspace is NULL or too small";
+    case FA_ERR_WORKSPACE: return "workspace is NULL or too small";
     case FA_ERR_SPLITS: return "num_splits out of range";
     case FA_ERR_HIP: return "HIP launch failed";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
@@ -208,6 +275,11 @@ const char* fa_fwd_kernel_name(int d, int causal, int Nq, int Nk) {
 
 const char* fa_decode_kernel_name(int d, int hq_per_kv, int stage) {
   return fa::decode_kernel_name(d, hq_per_kv, stage);
+}
+
+const char* fa_bwd_kernel_name(int d, int causal, int stage) {
+  if (causal != 0 && causal != 1) return nullptr;
+  return fa::bwd_kernel_name(d, causal != 0, stage);
 }
 
 }  // extern "C"

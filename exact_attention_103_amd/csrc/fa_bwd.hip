@@ -1,0 +1,533 @@
+// Exact attention backward for gfx950 (CDNA4, wave64, bf16 MFMA).
+//
+// Pages cited (short names):
+//   [Comparison] "FlashAttention 1-4 generation comparison"
+//                (phantomic12.github.io, inference-research)
+//   [Evolution]  "FlashAttention evolution" (sandeep007734.github.io,
+//                posts/flashattention-evolution)
+//
+// Gradients of the forward's output O for a loss whose gradient with respect
+// to O is dO.  As the pages describe for the backward pass ([Comparison]
+// "Notes", FlashAttention-1 entry: recompute instead of store), the
+// probabilities are rebuilt from Q, K and the forward's per-row LSE; nothing
+// of size N x N is ever stored.  With S = scale Q K^T (masked entries have
+// P = 0) and P = exp(S - LSE):
+//   dV = P^T dO     dP = dO V^T     dS = P (dP - Delta),  Delta = rowsum(dO * O)
+//   dQ = scale dS K                 dK = scale dS^T Q
+// Two kernels and no atomics, so results are deterministic:
+//   fa_bwd_dq_*    one workgroup of 4 waves per (128-row query block,
+//                  batch*head).  Each wave owns 32 query rows: it computes
+//                  Delta for them (stored for the second kernel), streams the
+//                  K/V tiles of its KV head through LDS and accumulates dQ in
+//                  registers (S^T, dP^T and dQ^T as in the forward: one query
+//                  per lane).
+//   fa_bwd_dkdv_*  one workgroup of 4 waves per (128-key block, batch*KV
+//                  head).  Each wave owns 32 keys whose K and V stay in
+//                  registers as MFMA B operands; it streams the Q/dO tiles of
+//                  every query head of the group and accumulates dK and dV
+//                  (S, dP with one key per lane; dV^T, dK^T).
+// In both kernels the bf16 probability / score-gradient registers feed the
+// next MFMA directly as its B operand (the contraction order is free), and
+// the transposed A operands (K^T, dO^T, Q^T) come from gfx950's transposing
+// LDS read on row-major tiles.
+
+#include "fa_internal.h"
+
+#include <math.h>
+
+namespace fa {
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// LDS layout of every bwd tile: 16-byte chunk c of row r sits at c ^ X(r),
+// X differing for any 16 consecutive rows (scaled for rows under 256 bytes),
+// so the row-major MFMA operand reads (16 lanes = 16 rows, same chunk) spread
+// over all banks.
+template <int RB>
+__device__ __forceinline__ int bwd_xor(int r) {
+  if constexpr (RB >= 256) return r & 15;
+  else return (r / (256 / RB)) & (RB / 16 - 1);
+}
+
+// Sum of lane l's and lane l ^ 32's values.
+__device__ __forceinline__ float lane_pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D>
+struct BwdShape {
+  static constexpr int RB = 2 * D;       // bytes per row in LDS
+  static constexpr int CPR = D / 8;      // 16-byte chunks per row
+  static constexpr int KSTEPS = D / 16;  // 32x32x16 k-steps over d
+  static constexpr int DB = D / 32;      // 32-wide d blocks of the transposed accumulators
+};
+
+constexpr int kBwdWaves = 4;
+constexpr int kDqRows = 32 * kBwdWaves;    // query rows per dQ workgroup
+constexpr int kDqKeys = 64;                // keys per K/V tile in the dQ kernel
+constexpr int kDkvKeys = 32 * kBwdWaves;   // keys per dK/dV workgroup
+constexpr int kDkvRows = 64;               // query rows per Q/dO tile in the dK/dV kernel
+
+// Direct global -> LDS copy of ROWS rows (from row r0, rows past nrows re-read
+// row nrows-1) of a row-major [.][D] bf16 matrix, swizzled with bwd_xor.
+// Wave load i writes 1 KB block i*NW + wave of the tile; lane l of it fetches
+// the global chunk whose swizzled position is that block's l-th chunk.
+template <int D, int ROWS>
+__device__ __forceinline__ void dma_rows(const uint16_t* base, int r0, int nrows, lds_char* tile,
+                                         int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int BLKS = ROWS * CPR / 64;
+  constexpr int LOADS = (BLKS + kBwdWaves - 1) / kBwdWaves;
+  static_assert((ROWS * CPR) % 64 == 0, "whole 1 KB blocks");
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int blk = i * kBwdWaves + wave;   // uniform across the wave
+    if (BLKS % kBwdWaves != 0 && blk >= BLKS) break;
+    const int P = blk * 64 + lane;
+    const int row = P / CPR;
+    const int c = (P % CPR) ^ bwd_xor<2 * D>(row);
+    const int r = min(r0 + row, nrows - 1);
+    __builtin_amdgcn_global_load_lds(base + (size_t)r * D + c * 8, tile + blk * 1024, 16, 0, 0);
+  }
+}
+
+// Byte offsets of the transposing reads of a 32-wide d block of a bwd tile,
+// for the rows 4*hl + (lane%16)/4 (+8 for the upper half) of every 16-row
+// group: lane (hl, g1, j16) receives, for k = 0..3, element d = 32*db + 16*g1
+// + j16 of rows 16*kc + 4*hl + k (+8).  Those are the rows (queries or keys)
+// that the B-operand registers 8*(kc%2).. of a transposed accumulator hold,
+// in the same order.  The XOR of a row depends only on the row within its
+// 16-row group, so one offset per (half, db) serves every group kc.
+template <int D>
+__device__ __forceinline__ void tr_offsets(int lane, int (&off)[2][BwdShape<D>::DB]) {
+  using S = BwdShape<D>;
+  const int hl = lane >> 5, g1 = (lane >> 4) & 1, j16 = lane & 15;
+  const int r0 = 4 * hl + (j16 >> 2);
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi) {
+    const int r = r0 + 8 * hi;
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db) {
+      const int c = 4 * db + 2 * g1 + ((j16 & 3) >> 1);
+      off[hi][db] = r * S::RB + ((c ^ bwd_xor<S::RB>(r)) << 4) + 8 * (j16 & 1);
+    }
+  }
+}
+
+__device__ __forceinline__ bf16x8 tr_read(const lds_char* t, int lo_off, int hi_off) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(t + lo_off));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(t + hi_off));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Row-major MFMA A operand: 8 bf16 of row r, logical chunk c, of a bwd tile.
+template <int RB>
+__device__ __forceinline__ bf16x8 row_read(const lds_char* t, int r, int c) {
+  return *(const __attribute__((address_space(3))) bf16x8*)(t + r * RB + ((c ^ bwd_xor<RB>(r)) << 4));
+}
+
+// ---------------------------------------------------------------------------
+// dQ (and Delta)
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void bwd_dq_body(const BwdParams& p, lds_char* kb0, lds_char* kb1,
+                                            lds_char* vb0, lds_char* vb1) {
+  using S = BwdShape<D>;
+  constexpr int BN = kDqKeys, BM = kDqRows;
+  constexpr int KB = BN / 32, KC = BN / 16;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int hl = lane >> 5;
+  const int n = lane & 31;
+
+  const int BH = p.B * p.Hq;
+  const int nqb = (p.Nq + BM - 1) / BM;
+  const int bh = blockIdx.x % BH;
+  const int qi = blockIdx.x / BH;
+  const int qblk = CAUSAL ? (nqb - 1 - qi) : qi;   // heaviest causal blocks first
+  const int b = bh / p.Hq;
+  const int h = bh - b * p.Hq;
+  const int g = h / p.group;
+  const int q0 = qblk * BM;
+  const int qw = q0 + 32 * wave;
+  const int row = qw + n;
+  const int off = p.Nk - p.Nq;                     // key j allowed for row i iff j <= i + off
+  const bool live = row < p.Nq;
+
+  const uint16_t* kbase = p.k + (size_t)(b * p.Hkv + g) * p.Nk * D;
+  const uint16_t* vbase = p.v + (size_t)(b * p.Hkv + g) * p.Nk * D;
+  const size_t rbase = ((size_t)bh * p.Nq + row) * D;
+
+  int nkt = (p.Nk + BN - 1) / BN;
+  if (CAUSAL) nkt = min(nkt, (min(q0 + BM, p.Nq) - 1 + off) / BN + 1);
+
+  // Q^T and dO^T as MFMA B operands (lane (hl, n): row `row`, d = 16t + 8hl
+  // .. +7), and Delta = rowsum(dO * O) in fp32.  Rows past Nq are zero.
+  bf16x8 qf[S::KSTEPS], df[S::KSTEPS];
+  float dsum = 0.f;
+#pragma unroll
+  for (int t = 0; t < S::KSTEPS; ++t) {
+    if (live) {
+      qf[t] = *reinterpret_cast<const bf16x8*>(p.q + rbase + 16 * t + 8 * hl);
+      df[t] = *reinterpret_cast<const bf16x8*>(p.dout + rbase + 16 * t + 8 * hl);
+      const bf16x8 ov = *reinterpret_cast<const bf16x8*>(p.o + rbase + 16 * t + 8 * hl);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum = fmaf((float)df[t][e], (float)ov[e], dsum);
+    } else {
+      qf[t] = bf16x8{};
+      df[t] = bf16x8{};
+    }
+  }
+  const float delta = lane_pair_sum(dsum);
+  const float nlse2 = live ? -p.lse[(size_t)bh * p.Nq + row] * kLog2e : 0.f;
+  if (live && hl == 0) p.delta[(size_t)bh * p.Nq + row] = delta;
+
+  const int koff = n * S::RB;
+  int toff[2][S::DB];
+  tr_offsets<D>(lane, toff);
+
+  f32x16 dq[S::DB];
+#pragma unroll
+  for (int db = 0; db < S::DB; ++db) dq[db] = f32x16{};
+
+  // X^T = T B^T for one 64-key tile T (K or V) and this wave's B (Q or dO).
+  auto xt_tile = [&](const lds_char* t, const bf16x8 (&bf)[S::KSTEPS], f32x16 (&acc)[KB]) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      acc[kb] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < S::KSTEPS; ++s)
+        acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            row_read<S::RB>(t, kb * 32 + n, 2 * s + hl), bf[s], acc[kb], 0, 0, 0);
+    }
+  };
+
+  auto step = [&](const lds_char* kr, const lds_char* vr, lds_char* kw, lds_char* vw, int j) {
+    const int j0 = j * BN;
+    if (j + 1 < nkt) {
+      dma_rows<D, BN>(kbase, j0 + BN, p.Nk, kw, wave, lane);
+      dma_rows<D, BN>(vbase, j0 + BN, p.Nk, vw, wave, lane);
+    }
+    f32x16 sacc[KB], dpacc[KB];
+    xt_tile(kr, qf, sacc);    // S^T  = K Q^T
+    xt_tile(vr, df, dpacc);   // dP^T = V dO^T
+    // Keys past Nk, or past the diagonal when causal, get P = 0.
+    if ((j0 + BN > p.Nk) || (CAUSAL && j0 + BN - 1 > qw + off)) {
+      const int lim = (CAUSAL ? min(p.Nk - 1, row + off) : p.Nk - 1) - j0 - 4 * hl;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
+    }
+    // Per 16-key chunk: dS^T = P^T (dP^T - Delta) as the bf16 B operand, then
+    // dQ^T += K^T dS^T with K^T from transposing reads of the K tile.
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      bf16x8 dsb;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * (kc & 1) + i;
+        const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[kc >> 1][r], p.c, nlse2));
+        dsb[i] = (__bf16)(pr * (dpacc[kc >> 1][r] - delta));
+      }
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db) {
+        const bf16x8 a = tr_read(kr, toff[0][db] + 16 * kc * S::RB, toff[1][db] + 16 * kc * S::RB);
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb, dq[db], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  };
+
+  dma_rows<D, BN>(kbase, 0, p.Nk, kb0, wave, lane);
+  dma_rows<D, BN>(vbase, 0, p.Nk, vb0, wave, lane);
+  __syncthreads();
+  for (int j = 0; j < nkt; j += 2) {
+    step(kb0, vb0, kb1, vb1, j);
+    if (j + 1 < nkt) step(kb1, vb1, kb0, vb0, j + 1);
+  }
+
+  // dQ = scale * acc, bf16 (round to nearest even); lane holds d rows
+  // 32db + 8(r/4) + 4hl + r%4 of its query row.
+  if (live) {
+    uint16_t* drow = p.dq + rbase;
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x2 lo = {(__bf16)(dq[db][4 * r4 + 0] * p.scale), (__bf16)(dq[db][4 * r4 + 1] * p.scale)};
+        bf16x2 hi = {(__bf16)(dq[db][4 * r4 + 2] * p.scale), (__bf16)(dq[db][4 * r4 + 3] * p.scale)};
+        uint2 w;
+        w.x = __builtin_bit_cast(unsigned, lo);
+        w.y = __builtin_bit_cast(unsigned, hi);
+        *reinterpret_cast<uint2*>(drow + 32 * db + 8 * r4 + 4 * hl) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV
+// ---------------------------------------------------------------------------
+// LDS per stage: Q tile, dO tile (kDkvRows rows each), then LSE and Delta of
+// those rows (fp32).
+template <int D>
+struct DkvStage {
+  static constexpr int TILE = kDkvRows * 2 * D;
+  static constexpr int STATS = 2 * kDkvRows * 4;
+};
+
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* qt0, lds_char* qt1,
+                                              lds_char* dt0, lds_char* dt1, lds_char* st0,
+                                              lds_char* st1) {
+  using S = BwdShape<D>;
+  constexpr int BM = kDkvRows, BNK = kDkvKeys;
+  constexpr int QB = BM / 32;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int hl = lane >> 5;
+  const int n = lane & 31;
+
+  const int BG = p.B * p.Hkv;
+  const int bg = blockIdx.x % BG;
+  const int kblk = blockIdx.x / BG;               // low key blocks see the most queries
+  const int b = bg / p.Hkv;
+  const int g = bg - b * p.Hkv;
+  const int k0 = kblk * BNK;
+  const int kw0 = k0 + 32 * wave;                 // first key of this wave
+  const int key = kw0 + n;
+  const int off = p.Nk - p.Nq;
+  const bool live = key < p.Nk;
+  const size_t kvrow = ((size_t)bg * p.Nk + key) * D;
+
+  // K^T and V^T of this lane's key as MFMA B operands (d = 16t + 8hl .. +7).
+  bf16x8 kf[S::KSTEPS], vf[S::KSTEPS];
+#pragma unroll
+  for (int t = 0; t < S::KSTEPS; ++t) {
+    kf[t] = live ? *reinterpret_cast<const bf16x8*>(p.k + kvrow + 16 * t + 8 * hl) : bf16x8{};
+    vf[t] = live ? *reinterpret_cast<const bf16x8*>(p.v + kvrow + 16 * t + 8 * hl) : bf16x8{};
+  }
+
+  // Query tiles: every query head of the group, rows from the first one that
+  // sees key k0 (causal) to Nq.
+  const int qstart = CAUSAL ? (max(0, k0 - off) / BM) * BM : 0;
+  const int nqt = (p.Nq - qstart + BM - 1) / BM;
+  const int steps = p.group * nqt;
+
+  int toff[2][S::DB];
+  tr_offsets<D>(lane, toff);
+
+  f32x16 dk[S::DB], dv[S::DB];
+#pragma unroll
+  for (int db = 0; db < S::DB; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  auto tile_head = [&](int s) { return g * p.group + s / nqt; };
+  auto tile_row = [&](int s) { return qstart + (s % nqt) * BM; };
+  auto load = [&](int s, lds_char* qt, lds_char* dt, lds_char* st) {
+    const int h = tile_head(s), i0 = tile_row(s);
+    const size_t hb = (size_t)(b * p.Hq + h) * p.Nq;
+    dma_rows<D, BM>(p.q + hb * D, i0, p.Nq, qt, wave, lane);
+    dma_rows<D, BM>(p.dout + hb * D, i0, p.Nq, dt, wave, lane);
+    if (wave < 2) {   // wave 0: LSE of the BM rows, wave 1: Delta
+      const float* src = wave == 0 ? p.lse + hb : p.delta + hb;
+#pragma unroll
+      for (int u = 0; u < BM / 64; ++u)
+        __builtin_amdgcn_global_load_lds(src + min(i0 + 64 * u + lane, p.Nq - 1),
+                                         st + wave * BM * 4 + u * 256, 4, 0, 0);
+    }
+  };
+
+  auto step = [&](const lds_char* qt, const lds_char* dt, const lds_char* st, lds_char* qw,
+                  lds_char* dw, lds_char* sw, int s) {
+    if (s + 1 < steps) load(s + 1, qw, dw, sw);
+    const int i0 = tile_row(s);
+    const __attribute__((address_space(3))) float* lse_t =
+        (const __attribute__((address_space(3))) float*)st;
+    const __attribute__((address_space(3))) float* del_t = lse_t + BM;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int rq = 32 * qb;   // first row of the 32-row block within the tile
+      // S = Q K^T and dP = dO V^T: one key per lane, rows 8(r/4) + 4hl + r%4.
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+      for (int t = 0; t < S::KSTEPS; ++t) {
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<S::RB>(qt, rq + n, 2 * t + hl),
+                                                       kf[t], sacc, 0, 0, 0);
+        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<S::RB>(dt, rq + n, 2 * t + hl),
+                                                        vf[t], dpacc, 0, 0, 0);
+      }
+      const int rfirst = i0 + rq;
+      if ((rfirst + 31 >= p.Nq) || (CAUSAL && kw0 + 31 > rfirst + off)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ri = rfirst + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (ri >= p.Nq || (CAUSAL && key > ri + off)) sacc[r] = -INFINITY;
+        }
+      }
+      // P = exp(S - LSE) in base 2, as bf16 B operands for dV^T += dO^T P.
+      float pr[16];
+      bf16x8 pb[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float l = lse_t[rq + 8 * (r >> 2) + 4 * hl + (r & 3)];
+        pr[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], p.c, -l * kLog2e));
+        pb[r >> 3][r & 7] = (__bf16)pr[r];
+      }
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+        for (int db = 0; db < S::DB; ++db) {
+          const int ro = (rq + 16 * kq) * S::RB;
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              tr_read(dt, toff[0][db] + ro, toff[1][db] + ro), pb[kq], dv[db], 0, 0, 0);
+        }
+      // dS = P (dP - Delta), as bf16 B operands for dK^T += Q^T dS.
+      bf16x8 sb[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float dl = del_t[rq + 8 * (r >> 2) + 4 * hl + (r & 3)];
+        sb[r >> 3][r & 7] = (__bf16)(pr[r] * (dpacc[r] - dl));
+      }
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+        for (int db = 0; db < S::DB; ++db) {
+          const int ro = (rq + 16 * kq) * S::RB;
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              tr_read(qt, toff[0][db] + ro, toff[1][db] + ro), sb[kq], dk[db], 0, 0, 0);
+        }
+    }
+    __syncthreads();
+  };
+
+  if (steps > 0) {
+    load(0, qt0, dt0, st0);
+    __syncthreads();
+  }
+  for (int s = 0; s < steps; s += 2) {
+    step(qt0, dt0, st0, qt1, dt1, st1, s);
+    if (s + 1 < steps) step(qt1, dt1, st1, qt0, dt0, st0, s + 1);
+  }
+
+  // dK = scale * acc, dV = acc, bf16; lane holds d rows 32db + 8(r/4) + 4hl
+  // + r%4 of its key.
+  if (live) {
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x2 klo = {(__bf16)(dk[db][4 * r4 + 0] * p.scale), (__bf16)(dk[db][4 * r4 + 1] * p.scale)};
+        bf16x2 khi = {(__bf16)(dk[db][4 * r4 + 2] * p.scale), (__bf16)(dk[db][4 * r4 + 3] * p.scale)};
+        bf16x2 vlo = {(__bf16)dv[db][4 * r4 + 0], (__bf16)dv[db][4 * r4 + 1]};
+        bf16x2 vhi = {(__bf16)dv[db][4 * r4 + 2], (__bf16)dv[db][4 * r4 + 3]};
+        uint2 wk, wv;
+        wk.x = __builtin_bit_cast(unsigned, klo);
+        wk.y = __builtin_bit_cast(unsigned, khi);
+        wv.x = __builtin_bit_cast(unsigned, vlo);
+        wv.y = __builtin_bit_cast(unsigned, vhi);
+        *reinterpret_cast<uint2*>(p.dk + kvrow + 32 * db + 8 * r4 + 4 * hl) = wk;
+        *reinterpret_cast<uint2*>(p.dv + kvrow + 32 * db + 8 * r4 + 4 * hl) = wv;
+      }
+  }
+}
+
+}  // namespace
+}  // namespace fa
+
+#define FA_BWD_DQ(D, CAUSAL, NAME)                                                         \
+  extern "C" __global__ void __launch_bounds__(64 * fa::kBwdWaves, 2) NAME(fa::BwdParams p) { \
+    constexpr int T = fa::kDqKeys * 2 * D;                                                 \
+    __shared__ __attribute__((aligned(1024))) char k0[T];                                  \
+    __shared__ __attribute__((aligned(1024))) char k1[T];                                  \
+    __shared__ __attribute__((aligned(1024))) char v0[T];                                  \
+    __shared__ __attribute__((aligned(1024))) char v1[T];                                  \
+    fa::bwd_dq_body<D, CAUSAL>(p, (fa::lds_char*)k0, (fa::lds_char*)k1, (fa::lds_char*)v0, \
+                               (fa::lds_char*)v1);                                         \
+  }
+
+#define FA_BWD_DKDV(D, CAUSAL, NAME)                                                       \
+  extern "C" __global__ void __launch_bounds__(64 * fa::kBwdWaves, 1) NAME(fa::BwdParams p) { \
+    using St = fa::DkvStage<D>;                                                            \
+    __shared__ __attribute__((aligned(1024))) char q0[St::TILE];                           \
+    __shared__ __attribute__((aligned(1024))) char q1[St::TILE];                           \
+    __shared__ __attribute__((aligned(1024))) char d0[St::TILE];                           \
+    __shared__ __attribute__((aligned(1024))) char d1[St::TILE];                           \
+    __shared__ __attribute__((aligned(256))) char s0[St::STATS];                           \
+    __shared__ __attribute__((aligned(256))) char s1[St::STATS];                           \
+    fa::bwd_dkdv_body<D, CAUSAL>(p, (fa::lds_char*)q0, (fa::lds_char*)q1,                  \
+                                 (fa::lds_char*)d0, (fa::lds_char*)d1,                     \
+                                 (fa::lds_char*)s0, (fa::lds_char*)s1);                    \
+  }
+
+FA_BWD_DQ(32, false, fa_bwd_dq_d32_nomask)
+FA_BWD_DQ(32, true, fa_bwd_dq_d32_causal)
+FA_BWD_DQ(64, false, fa_bwd_dq_d64_nomask)
+FA_BWD_DQ(64, true, fa_bwd_dq_d64_causal)
+FA_BWD_DQ(128, false, fa_bwd_dq_d128_nomask)
+FA_BWD_DQ(128, true, fa_bwd_dq_d128_causal)
+FA_BWD_DKDV(32, false, fa_bwd_dkdv_d32_nomask)
+FA_BWD_DKDV(32, true, fa_bwd_dkdv_d32_causal)
+FA_BWD_DKDV(64, false, fa_bwd_dkdv_d64_nomask)
+FA_BWD_DKDV(64, true, fa_bwd_dkdv_d64_causal)
+FA_BWD_DKDV(128, false, fa_bwd_dkdv_d128_nomask)
+FA_BWD_DKDV(128, true, fa_bwd_dkdv_d128_causal)
+
+namespace fa {
+
+bool bwd_supported_d(int d) { return d == 32 || d == 64 || d == 128; }
+
+int bwd_dq_grid_blocks(int B, int Hq, int Nq) { return ((Nq + kDqRows - 1) / kDqRows) * B * Hq; }
+int bwd_dkdv_grid_blocks(int B, int Hkv, int Nk) {
+  return ((Nk + kDkvKeys - 1) / kDkvKeys) * B * Hkv;
+}
+
+const char* bwd_kernel_name(int d, bool causal, int stage) {
+  static const char* const names[2][3][2] = {
+      {{"fa_bwd_dq_d32_nomask", "fa_bwd_dq_d32_causal"},
+       {"fa_bwd_dq_d64_nomask", "fa_bwd_dq_d64_causal"},
+       {"fa_bwd_dq_d128_nomask", "fa_bwd_dq_d128_causal"}},
+      {{"fa_bwd_dkdv_d32_nomask", "fa_bwd_dkdv_d32_causal"},
+       {"fa_bwd_dkdv_d64_nomask", "fa_bwd_dkdv_d64_causal"},
+       {"fa_bwd_dkdv_d128_nomask", "fa_bwd_dkdv_d128_causal"}}};
+  if (stage != 0 && stage != 1) return nullptr;
+  const int di = d == 32 ? 0 : d == 64 ? 1 : d == 128 ? 2 : -1;
+  if (di < 0) return nullptr;
+  return names[stage][di][causal ? 1 : 0];
+}
+
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s) {
+  const void* f1 = nullptr;
+  const void* f2 = nullptr;
+#define FA_PICK(D)                                                                       \
+  case D:                                                                                \
+    f1 = causal ? (const void*)fa_bwd_dq_d##D##_causal : (const void*)fa_bwd_dq_d##D##_nomask; \
+    f2 = causal ? (const void*)fa_bwd_dkdv_d##D##_causal : (const void*)fa_bwd_dkdv_d##D##_nomask; \
+    break;
+  switch (d) {
+    FA_PICK(32)
+    FA_PICK(64)
+    FA_PICK(128)
+    default: return hipErrorInvalidValue;
+  }
+#undef FA_PICK
+  BwdParams arg = p;
+  void* args[] = {&arg};
+  const dim3 block(64 * kBwdWaves);
+  // The dQ kernel writes Delta, which the dK/dV kernel reads: stream order.
+  hipError_t e = hipLaunchKernel(f1, dim3(bwd_dq_grid_blocks(p.B, p.Hq, p.Nq)), block, args, 0, s);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel(f2, dim3(bwd_dkdv_grid_blocks(p.B, p.Hkv, p.Nk)), block, args, 0, s);
+}
+
+}  // namespace fa

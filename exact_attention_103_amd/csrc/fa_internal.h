@@ -45,12 +45,36 @@ struct DecodeParams {
   float c;                // scale * log2(e)
 };
 
+// Arguments of one backward call (dQ kernel, then dK/dV kernel).  Tensors
+// are [B][H][N][d] bf16; lse and delta are [B][Hq][Nq] fp32.
+struct BwdParams {
+  const uint16_t* q;      // [B][Hq][Nq][d]
+  const uint16_t* k;      // [B][Hkv][Nk][d]
+  const uint16_t* v;
+  const uint16_t* o;      // forward output
+  const uint16_t* dout;   // gradient of the loss with respect to o
+  const float* lse;       // forward LSE, natural log
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* delta;           // rowsum(dout * o): written by the dQ kernel, read by dK/dV
+  int B, Hq, Hkv, Nq, Nk;
+  int group;              // Hq / Hkv
+  float c;                // scale * log2(e)
+  float scale;
+};
+
 // Host-side launchers (defined next to their kernels).  They assume the
 // arguments were validated and return the hipError_t of the launch.
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t s);
 const char* fwd_kernel_name(int d, bool causal, int Nq, int Nk);
 const char* decode_kernel_name(int d, int group, int stage);
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s);
+const char* bwd_kernel_name(int d, bool causal, int stage);
+bool bwd_supported_d(int d);
+int bwd_dq_grid_blocks(int B, int Hq, int Nq);
+int bwd_dkdv_grid_blocks(int B, int Hkv, int Nk);
 
 // Tile shape of the forward kernel that runs for a problem (BM query rows
 // per workgroup, BN keys per tile, waves per workgroup).

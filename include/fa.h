@@ -7,6 +7,8 @@
  *                posts/flashattention-evolution)
  *   [Kruglikov]  "Flash Attention" (vladislavkruglikov.com,
  *                articles/flash-attention)
+ *   [Comparison] "FlashAttention 1-4 generation comparison"
+ *                (phantomic12.github.io, inference-research)
  *
  * Conventions shared by every entry point
  *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
@@ -37,9 +39,9 @@ enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = -1,       /* a required pointer is NULL                      */
   FA_ERR_SHAPE = -2,      /* B, H or N <= 0, Hq % Hkv != 0, causal && Nq > Nk */
-  FA_ERR_HEAD_DIM = -3,   /* d not in {32, 64, 128, 256}                     */
+  FA_ERR_HEAD_DIM = -3,   /* d not in {32, 64, 128, 256} ({32, 64, 128} bwd) */
   FA_ERR_ALIGN = -4,      /* a tensor pointer is not 16-byte aligned         */
-  FA_ERR_WORKSPACE = -5,  /* decode workspace NULL or smaller than required  */
+  FA_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required         */
   FA_ERR_SPLITS = -6,     /* num_splits outside 0 .. fa_decode_max_splits()  */
   FA_ERR_HIP = -7,        /* a HIP launch failed; see fa_last_hip_error()    */
   FA_ERR_SCALE = -8,      /* scale not finite or not > 0                     */
@@ -120,6 +122,44 @@ int fa_decode_num_splits(int B, int Hq, int Hkv, int Nk, int d);
 /* Largest accepted num_splits for a cache of Nk keys: ceil(Nk / 64). */
 int fa_decode_max_splits(int Nk);
 
+/*
+ * fa_bwd -- gradients of fa_fwd's output.
+ *
+ * For a loss whose gradient with respect to O is dO, computes with
+ * P = exp(S - LSE), S = scale * Q K^T (masked keys: P = 0, as in fa_fwd):
+ *   dV = P^T dO,  dP = dO V^T,  dS = P (dP - Delta),  Delta_i = dO_i . O_i,
+ *   dQ = scale * dS K,  dK = scale * dS^T Q,
+ * grouped-query heads summing into their shared KV head's dK, dV.  The pages
+ * print no gradient formulas: these are the chain rule applied to fa_fwd's
+ * function.  As [Comparison] "Notes" (FlashAttention-1 entry) describes for
+ * the backward pass, the probabilities are recomputed from Q, K and the
+ * forward's LSE instead of being stored.
+ *
+ *   q, o, dout bf16 [B][Hq][Nq][d]     (o: fa_fwd's output; dout: dL/dO)
+ *   k, v       bf16 [B][Hkv][Nk][d]
+ *   lse        fp32 [B][Hq][Nq]        fa_fwd's LSE (natural log)
+ *   dq         bf16 [B][Hq][Nq][d]     output
+ *   dk, dv     bf16 [B][Hkv][Nk][d]    outputs
+ *   d          32, 64 or 128
+ *   scale, causal  the values the forward used
+ *   workspace  device scratch of at least fa_bwd_workspace_size(B, Hq, Nq)
+ *              bytes (Delta, fp32), 16-byte aligned, owned by the caller; it
+ *              must not overlap any tensor argument.  Contents on return are
+ *              unspecified.
+ * Two kernels run in stream order (dQ and Delta, then dK and dV); there are
+ * no atomics, so repeated calls give identical bits.
+ * Returns FA_OK or a negative fa_status (FA_ERR_WORKSPACE for a NULL or
+ * short workspace, FA_ERR_ALIAS if an output or the workspace overlaps an
+ * input or another output).
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv,
+           int Nq, int Nk, int d, float scale, int causal, void* workspace,
+           size_t workspace_bytes, void* stream);
+
+/* Bytes of backward workspace: 4*B*Hq*Nq (Delta, fp32).  0 on invalid sizes. */
+size_t fa_bwd_workspace_size(int B, int Hq, int Nq);
+
 /* Static text for a status code. */
 const char* fa_strerror(int status);
 
@@ -134,6 +174,9 @@ const char* fa_last_hip_error(void);
  * query heads per KV head), stage 1 = merge kernel. */
 const char* fa_fwd_kernel_name(int d, int causal, int Nq, int Nk);
 const char* fa_decode_kernel_name(int d, int hq_per_kv, int stage);
+/* fa_bwd_kernel_name: stage 0 = dQ kernel (also writes Delta), stage 1 =
+ * dK/dV kernel. */
+const char* fa_bwd_kernel_name(int d, int causal, int stage);
 
 #ifdef __cplusplus
 }

@@ -64,3 +64,39 @@ def assert_parity(tag, o, lse, o_ref, lse_ref):
 def announce(msg):
     print(f"[gpu-case] {msg}", flush=True)
     sys.stdout.flush()
+
+
+# Gradients.  Each element of dQ, dK, dV is a sum over keys or query rows of
+# products whose bf16 operands (P, dS) carry independent rounding of relative
+# size <= 2^-9, plus the bf16 rounding of the result and of the forward
+# output O that Delta = rowsum(dO * O) is computed from.  Those roundings give
+# a relative Frobenius error of a few times 2^-9 / sqrt(3) ~ 1e-3; the bar
+# allows about 5 * 2^-9:
+GRAD_REL_FRO = 1e-2      # ||G - G_ref||_F / ||G_ref||_F
+GRAD_MAX_REL = 3e-2      # max |G - G_ref| / max |G_ref|
+
+
+def report_grad(tag, name, g, g_ref):
+    g = np.asarray(g, dtype=np.float64)
+    g_ref = np.asarray(g_ref, dtype=np.float64)
+    diff = g - g_ref
+    ref_fro = float(np.sqrt((g_ref ** 2).sum()))
+    ref_max = float(np.abs(g_ref).max()) if g_ref.size else 0.0
+    rel_fro = float(np.sqrt((diff ** 2).sum())) / ref_fro if ref_fro > 0 else float(np.abs(diff).max())
+    max_rel = float(np.abs(diff).max()) / ref_max if ref_max > 0 else float(np.abs(diff).max())
+    finite = bool(np.all(np.isfinite(g)))
+    print(f"[parity] {tag} d{name}: rel-Frobenius {rel_fro:.3e} | max/max|ref| {max_rel:.3e} "
+          f"| max|ref| {ref_max:.3e} | finite {finite}", flush=True)
+    return dict(rel_fro=rel_fro, max_rel=max_rel, finite=finite)
+
+
+def assert_grad_parity(tag, grads, refs):
+    """grads, refs: dicts name -> array (dQ, dK, dV)."""
+    out = {}
+    for name in refs:
+        r = report_grad(tag, name, grads[name], refs[name])
+        assert r["finite"], f"{tag} d{name}: non-finite"
+        assert r["rel_fro"] <= GRAD_REL_FRO, f"{tag} d{name}: rel-Frobenius {r['rel_fro']:.3e}"
+        assert r["max_rel"] <= GRAD_MAX_REL, f"{tag} d{name}: max rel {r['max_rel']:.3e}"
+        out[name] = r
+    return out

@@ -82,6 +82,19 @@ def test_kernel_names():
     assert fa.fa_decode_kernel_name(48, 4, 0) is None
 
 
+def test_bwd_kernel_names_and_workspace():
+    for d in (32, 64, 128):
+        assert fa.fa_bwd_kernel_name(d, 0, 0) == f"fa_bwd_dq_d{d}_nomask"
+        assert fa.fa_bwd_kernel_name(d, 1, 0) == f"fa_bwd_dq_d{d}_causal"
+        assert fa.fa_bwd_kernel_name(d, 0, 1) == f"fa_bwd_dkdv_d{d}_nomask"
+        assert fa.fa_bwd_kernel_name(d, 1, 1) == f"fa_bwd_dkdv_d{d}_causal"
+    assert fa.fa_bwd_kernel_name(256, 0, 0) is None
+    assert fa.fa_bwd_kernel_name(128, 0, 2) is None
+    assert fa.fa_bwd_kernel_name(128, 2, 0) is None
+    assert fa.fa_bwd_workspace_size(2, 4, 100) == 4 * 2 * 4 * 100
+    assert fa.fa_bwd_workspace_size(0, 4, 100) == 0
+
+
 def test_workspace_and_splits():
     assert fa.fa_decode_workspace_size(8, 32, 128, 32) == 4 * 8 * 32 * 32 * 129
     assert fa.fa_decode_workspace_size(8, 32, 100, 32) == 0
@@ -166,3 +179,35 @@ def test_decode_exact_workspace_is_enough_and_heuristic_checked():
     # S = 0 picks the heuristic and checks the workspace against it.
     s0 = fa.fa_decode_num_splits(2, 8, 2, 1000, 128)
     assert _dec(S=0, ws_bytes=fa.fa_decode_workspace_size(2, 8, 128, s0) - 1) == -5
+
+
+# Backward: placeholder addresses again, one more per tensor.
+BQ, BK, BV, BO, BDO, BL, BDQ, BDK, BDV, BW = (0x1000000 * (i + 1) for i in range(10))
+GOOD_BWD = dict(q=BQ, k=BK, v=BV, o=BO, do=BDO, lse=BL, dq=BDQ, dk=BDK, dv=BDV, B=1, Hq=4,
+                Hkv=2, Nq=64, Nk=64, d=64, scale=0.125, causal=1, ws=BW, ws_bytes=1 << 20)
+
+
+def _bwd(**kw):
+    a = dict(GOOD_BWD)
+    a.update(kw)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"],
+                     a["dv"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                     a["causal"], a["ws"], a["ws_bytes"], None)
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), -1), (dict(k=0), -1), (dict(v=0), -1), (dict(o=0), -1), (dict(do=0), -1),
+    (dict(lse=0), -1), (dict(dq=0), -1), (dict(dk=0), -1), (dict(dv=0), -1),
+    (dict(B=0), -2), (dict(Hq=3), -2), (dict(Nq=0), -2), (dict(causal=2), -2),
+    (dict(Nq=65, Nk=64), -2),
+    (dict(d=256), -3), (dict(d=48), -3),
+    (dict(scale=0.0), -8), (dict(scale=math.inf), -8),
+    (dict(ws=0), -5), (dict(ws_bytes=4 * 4 * 64 - 1), -5),
+    (dict(q=BQ + 8), -4), (dict(dk=BDK + 2), -4), (dict(ws=BW + 4), -4),
+    (dict(dq=BQ), -9), (dict(dk=BV + 64), -9), (dict(dv=BDK), -9), (dict(ws=BL), -9),
+    (dict(dq=BDO + 16), -9), (dict(ws=BDV), -9),
+    (dict(B=1 << 20, Hq=1 << 10, Hkv=1 << 10, Nq=1 << 20, Nk=1 << 20, ws_bytes=1 << 62), -10),
+])
+def test_bwd_rejects(kw, code):
+    assert _bwd(**kw) == code
