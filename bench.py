@@ -12,8 +12,13 @@ same stream, inputs already resident in HBM.  Prints one JSON line:
             decode carries its own roofline against 8 TB/s HBM
   cpu_baseline  the float64 oracle on a bounded sample of the same workload,
             timed on the host cores (rank 0, one GPU)
+  bwd       after the timed steps: the backward pass (fa_bwd) of the same
+            prefill, fed the last step's O and LSE and a seeded dO, timed
+            over its own launches; TFLOP/s counts the algorithmic 5 products
+            of the backward (10*B*H*N*N*d / 2 flop, causal), not the 7 the
+            recomputation performs
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bwd]
 """
 
 from __future__ import annotations
@@ -96,6 +101,23 @@ def cpu_baseline_decode(cfg, qb, kb, vb, batches=8):
                 sample=f"float64 oracle, {batches} of {cfg.B} sequences of the decode workload")
 
 
+def cpu_baseline_bwd(cfg, qb, kb, vb, dob, head=0):
+    """Oracle gradients (dQ of every row, dK and dV of every key) of one head
+    of the prefill workload; throughput counts the algorithmic backward flop
+    of that head."""
+    import oracle
+    sel = lambda bits: datagen.f64_from_bf16_bits(bits[0, head])
+    t0 = time.perf_counter()
+    oracle.attention_bwd_head_ref(sel(qb), sel(kb), sel(vb), sel(dob), cfg.scale, cfg.causal)
+    dt = time.perf_counter() - t0
+    flop = 10.0 * cfg.Nq * cfg.Nk * cfg.d / (2 if cfg.causal else 1)
+    return dict(value=flop / dt / 1e12, unit="TFLOP/s", cores=_blas_threads(), kind="oracle",
+                seconds=round(dt, 3),
+                sample=f"float64 oracle gradients of head {head} of the causal B={cfg.B} "
+                       f"H={cfg.Hq} N={cfg.Nq} d={cfg.d} prefill (all rows and keys), "
+                       f"score, probability and gradient blocks materialised")
+
+
 def _blas_threads():
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
         if os.environ.get(var):
@@ -106,6 +128,49 @@ def _blas_threads():
     return os.cpu_count()
 
 
+def bwd_leg(fa, cfg, q, k, v, o, lse, stream, steps, warmup=10):
+    """Backward of the prefill: fa_bwd fed the forward's O and LSE and a
+    seeded dO, timed per call with HIP events on the launch stream."""
+    import torch
+    _, _, _, dob = datagen.make_bwd_inputs(cfg)
+    do = _dev(dob)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_size(cfg.B, cfg.Hq, cfg.Nq), dtype=torch.uint8,
+                     device="cuda")
+    sp = stream.cuda_stream
+
+    def call():
+        rc = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cfg.B,
+                       cfg.Hq, cfg.Hkv, cfg.Nq, cfg.Nk, cfg.d, cfg.scale, int(cfg.causal),
+                       ws.data_ptr(), ws.numel(), sp)
+        if rc:
+            raise fa.FAError(rc, "fa_bwd")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in evs:
+        e[0].record(stream)
+        call()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[1]) for e in evs]
+    b_ms = float(np.mean(ms))
+    flop = 2.5 * cfg.flops()
+    tf = flop / (b_ms * 1e-3) / 1e12
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(b_ms, 4),
+            "ms_min": round(min(ms), 4), "flop": flop,
+            "kernels": [fa.fa_bwd_kernel_name(cfg.d, int(cfg.causal), 0),
+                        fa.fa_bwd_kernel_name(cfg.d, int(cfg.causal), 1)],
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +178,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)   # ~70 ms: the clocks ramp up first
     ap.add_argument("--splits", type=int, default=0, help="decode splits (0 = heuristic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="instead of the benchmark, run three plain device-to-device "
                          "copies of BYTES bytes (reference dispatches for HBM counters)")
@@ -238,9 +304,14 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not args.no_bwd:
+        out["bwd"] = bwd_leg(fa, fcfg, q, k, v, o, lse, stream, args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_fwd(fcfg, fq, fk, fv)
         out["decode"]["cpu_baseline"] = cpu_baseline_decode(dcfg, dq, dk, dv)
+        if not args.no_bwd:
+            _, _, _, fdo = datagen.make_bwd_inputs(fcfg)
+            out["bwd"]["cpu_baseline"] = cpu_baseline_bwd(fcfg, fq, fk, fv, fdo)
     print(json.dumps(out), flush=True)
 
 
