@@ -69,7 +69,7 @@ constexpr int kBwdWaves = 4;
 constexpr int kDqRows = 32 * kBwdWaves;    // query rows per dQ workgroup
 constexpr int kDqKeys = 64;                // keys per K/V tile in the dQ kernel
 constexpr int kDkvKeys = 32 * kBwdWaves;   // keys per dK/dV workgroup
-constexpr int kDkvRows = 64;               // query rows per Q/dO tile in the dK/dV kernel
+constexpr int kDkvRows = 32;               // query rows per Q/dO tile in the dK/dV kernel
 
 // Direct global -> LDS copy of ROWS rows (from row r0, rows past nrows re-read
 // row nrows-1) of a row-major [.][D] bf16 matrix, swizzled with bwd_xor.
@@ -275,21 +275,23 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, lds_char* kb0, l
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
-// LDS per stage: Q tile, dO tile (kDkvRows rows each), then LSE and Delta of
-// those rows (fp32).
+// LDS: the workgroup's K block (kDkvKeys rows, read as MFMA B operands) and,
+// per stage, a Q tile, a dO tile (kDkvRows rows each) and the LSE and Delta
+// of those rows (fp32).
 template <int D>
 struct DkvStage {
+  static constexpr int KBLOCK = kDkvKeys * 2 * D;
   static constexpr int TILE = kDkvRows * 2 * D;
   static constexpr int STATS = 2 * kDkvRows * 4;
 };
 
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* qt0, lds_char* qt1,
-                                              lds_char* dt0, lds_char* dt1, lds_char* st0,
-                                              lds_char* st1) {
+__device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* kblock,
+                                              lds_char* qt0, lds_char* qt1, lds_char* dt0,
+                                              lds_char* dt1, lds_char* st0, lds_char* st1) {
   using S = BwdShape<D>;
   constexpr int BM = kDkvRows, BNK = kDkvKeys;
-  constexpr int QB = BM / 32;
+  static_assert(BM == 32, "one 32-row block per stage");
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -306,15 +308,16 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* qt0,
   const int key = kw0 + n;
   const int off = p.Nk - p.Nq;
   const bool live = key < p.Nk;
+  const uint16_t* kbase = p.k + (size_t)bg * p.Nk * D;
   const size_t kvrow = ((size_t)bg * p.Nk + key) * D;
 
-  // K^T and V^T of this lane's key as MFMA B operands (d = 16t + 8hl .. +7).
-  bf16x8 kf[S::KSTEPS], vf[S::KSTEPS];
+  // V^T of this lane's key as MFMA B operands (d = 16t + 8hl .. +7); K^T is
+  // read from the K block in LDS with the same layout (rows 32*wave + n).
+  bf16x8 vf[S::KSTEPS];
 #pragma unroll
-  for (int t = 0; t < S::KSTEPS; ++t) {
-    kf[t] = live ? *reinterpret_cast<const bf16x8*>(p.k + kvrow + 16 * t + 8 * hl) : bf16x8{};
+  for (int t = 0; t < S::KSTEPS; ++t)
     vf[t] = live ? *reinterpret_cast<const bf16x8*>(p.v + kvrow + 16 * t + 8 * hl) : bf16x8{};
-  }
+  dma_rows<D, BNK>(kbase, k0, p.Nk, kblock, wave, lane);
 
   // Query tiles: every query head of the group, rows from the first one that
   // sees key k0 (causal) to Nq.
@@ -332,19 +335,16 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* qt0,
     dv[db] = f32x16{};
   }
 
-  auto tile_head = [&](int s) { return g * p.group + s / nqt; };
   auto tile_row = [&](int s) { return qstart + (s % nqt) * BM; };
   auto load = [&](int s, lds_char* qt, lds_char* dt, lds_char* st) {
-    const int h = tile_head(s), i0 = tile_row(s);
+    const int h = g * p.group + s / nqt, i0 = tile_row(s);
     const size_t hb = (size_t)(b * p.Hq + h) * p.Nq;
     dma_rows<D, BM>(p.q + hb * D, i0, p.Nq, qt, wave, lane);
     dma_rows<D, BM>(p.dout + hb * D, i0, p.Nq, dt, wave, lane);
-    if (wave < 2) {   // wave 0: LSE of the BM rows, wave 1: Delta
-      const float* src = wave == 0 ? p.lse + hb : p.delta + hb;
-#pragma unroll
-      for (int u = 0; u < BM / 64; ++u)
-        __builtin_amdgcn_global_load_lds(src + min(i0 + 64 * u + lane, p.Nq - 1),
-                                         st + wave * BM * 4 + u * 256, 4, 0, 0);
+    if (wave == 0) {   // lanes 0-31: LSE of the BM rows, lanes 32-63: Delta
+      const float* src = (lane < BM ? p.lse : p.delta - BM) + hb;
+      __builtin_amdgcn_global_load_lds(src + min(i0 + (lane & (BM - 1)), p.Nq - 1) + (lane & BM),
+                                       st, 4, 0, 0);
     }
   };
 
@@ -355,66 +355,62 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* qt0,
     const __attribute__((address_space(3))) float* lse_t =
         (const __attribute__((address_space(3))) float*)st;
     const __attribute__((address_space(3))) float* del_t = lse_t + BM;
+
+    // S = Q K^T: one key per lane, rows 8(r/4) + 4hl + r%4 of the tile.
+    f32x16 sacc = f32x16{};
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int rq = 32 * qb;   // first row of the 32-row block within the tile
-      // S = Q K^T and dP = dO V^T: one key per lane, rows 8(r/4) + 4hl + r%4.
-      f32x16 sacc = f32x16{}, dpacc = f32x16{};
-#pragma unroll
-      for (int t = 0; t < S::KSTEPS; ++t) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<S::RB>(qt, rq + n, 2 * t + hl),
-                                                       kf[t], sacc, 0, 0, 0);
-        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<S::RB>(dt, rq + n, 2 * t + hl),
-                                                        vf[t], dpacc, 0, 0, 0);
-      }
-      const int rfirst = i0 + rq;
-      if ((rfirst + 31 >= p.Nq) || (CAUSAL && kw0 + 31 > rfirst + off)) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ri = rfirst + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (ri >= p.Nq || (CAUSAL && key > ri + off)) sacc[r] = -INFINITY;
-        }
-      }
-      // P = exp(S - LSE) in base 2, as bf16 B operands for dV^T += dO^T P.
-      float pr[16];
-      bf16x8 pb[2];
+    for (int t = 0; t < S::KSTEPS; ++t)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<S::RB>(qt, n, 2 * t + hl),
+                                                     row_read<S::RB>(kblock, 32 * wave + n, 2 * t + hl),
+                                                     sacc, 0, 0, 0);
+    if ((i0 + 31 >= p.Nq) || (CAUSAL && kw0 + 31 > i0 + off)) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float l = lse_t[rq + 8 * (r >> 2) + 4 * hl + (r & 3)];
-        pr[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], p.c, -l * kLog2e));
-        pb[r >> 3][r & 7] = (__bf16)pr[r];
+        const int ri = i0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        if (ri >= p.Nq || (CAUSAL && key > ri + off)) sacc[r] = -INFINITY;
       }
-#pragma unroll
-      for (int kq = 0; kq < 2; ++kq)
-#pragma unroll
-        for (int db = 0; db < S::DB; ++db) {
-          const int ro = (rq + 16 * kq) * S::RB;
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              tr_read(dt, toff[0][db] + ro, toff[1][db] + ro), pb[kq], dv[db], 0, 0, 0);
-        }
-      // dS = P (dP - Delta), as bf16 B operands for dK^T += Q^T dS.
-      bf16x8 sb[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float dl = del_t[rq + 8 * (r >> 2) + 4 * hl + (r & 3)];
-        sb[r >> 3][r & 7] = (__bf16)(pr[r] * (dpacc[r] - dl));
-      }
-#pragma unroll
-      for (int kq = 0; kq < 2; ++kq)
-#pragma unroll
-        for (int db = 0; db < S::DB; ++db) {
-          const int ro = (rq + 16 * kq) * S::RB;
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              tr_read(qt, toff[0][db] + ro, toff[1][db] + ro), sb[kq], dk[db], 0, 0, 0);
-        }
     }
+    // P = exp(S - LSE) in base 2, rounded to bf16: the B operand of
+    // dV^T += dO^T P, and the P of dS below.
+    bf16x8 pb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float l = lse_t[8 * (r >> 2) + 4 * hl + (r & 3)];
+      pb[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[r], p.c, -l * kLog2e));
+    }
+#pragma unroll
+    for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db) {
+        const int ro = 16 * kq * S::RB;
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tr_read(dt, toff[0][db] + ro, toff[1][db] + ro), pb[kq], dv[db], 0, 0, 0);
+      }
+    // dP = dO V^T, then dS = P (dP - Delta) as the B operand of dK^T += Q^T dS.
+    f32x16 dpacc = f32x16{};
+#pragma unroll
+    for (int t = 0; t < S::KSTEPS; ++t)
+      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<S::RB>(dt, n, 2 * t + hl), vf[t],
+                                                      dpacc, 0, 0, 0);
+    bf16x8 sb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float dl = del_t[8 * (r >> 2) + 4 * hl + (r & 3)];
+      sb[r >> 3][r & 7] = (__bf16)((float)pb[r >> 3][r & 7] * (dpacc[r] - dl));
+    }
+#pragma unroll
+    for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db) {
+        const int ro = 16 * kq * S::RB;
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tr_read(qt, toff[0][db] + ro, toff[1][db] + ro), sb[kq], dk[db], 0, 0, 0);
+      }
     __syncthreads();
   };
 
-  if (steps > 0) {
-    load(0, qt0, dt0, st0);
-    __syncthreads();
-  }
+  load(0, qt0, dt0, st0);
+  __syncthreads();
   for (int s = 0; s < steps; s += 2) {
     step(qt0, dt0, st0, qt1, dt1, st1, s);
     if (s + 1 < steps) step(qt1, dt1, st1, qt0, dt0, st0, s + 1);
@@ -457,15 +453,16 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* qt0,
   }
 
 #define FA_BWD_DKDV(D, CAUSAL, NAME)                                                       \
-  extern "C" __global__ void __launch_bounds__(64 * fa::kBwdWaves, 1) NAME(fa::BwdParams p) { \
+  extern "C" __global__ void __launch_bounds__(64 * fa::kBwdWaves, 2) NAME(fa::BwdParams p) { \
     using St = fa::DkvStage<D>;                                                            \
+    __shared__ __attribute__((aligned(1024))) char kb[St::KBLOCK];                         \
     __shared__ __attribute__((aligned(1024))) char q0[St::TILE];                           \
     __shared__ __attribute__((aligned(1024))) char q1[St::TILE];                           \
     __shared__ __attribute__((aligned(1024))) char d0[St::TILE];                           \
     __shared__ __attribute__((aligned(1024))) char d1[St::TILE];                           \
     __shared__ __attribute__((aligned(256))) char s0[St::STATS];                           \
     __shared__ __attribute__((aligned(256))) char s1[St::STATS];                           \
-    fa::bwd_dkdv_body<D, CAUSAL>(p, (fa::lds_char*)q0, (fa::lds_char*)q1,                  \
+    fa::bwd_dkdv_body<D, CAUSAL>(p, (fa::lds_char*)kb, (fa::lds_char*)q0, (fa::lds_char*)q1, \
                                  (fa::lds_char*)d0, (fa::lds_char*)d1,                     \
                                  (fa::lds_char*)s0, (fa::lds_char*)s1);                    \
   }
