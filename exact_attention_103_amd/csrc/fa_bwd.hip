@@ -42,14 +42,26 @@ namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-// LDS layout of every bwd tile: 16-byte chunk c of row r sits at c ^ X(r),
-// X differing for any 16 consecutive rows (scaled for rows under 256 bytes),
-// so the row-major MFMA operand reads (16 lanes = 16 rows, same chunk) spread
-// over all banks.
+// LDS layout of every bwd tile: 16-byte chunk c of row r sits at c ^ X(r).
+// Every tile is read two ways, and X serves both:
+//  * row-major MFMA operands: 16 lanes read one chunk of 16 consecutive rows,
+//    so X must take a different value on each row that shares a 256-byte
+//    bank line position (X is a bijection on r mod 16 for 256-byte rows);
+//  * transposing reads: a 16-lane group reads 4 consecutive chunks of 4
+//    consecutive rows, so those rows must land in different 64-byte bank
+//    groups (bits 2..3 of X differ between rows that share a line half).
+// For 256-byte rows X swaps the two 2-bit digits of r mod 16; for 128-byte
+// rows (two per line) it does the same on the row's line index; 64-byte rows
+// fill a line with four different rows and need only the first property.
 template <int RB>
 __device__ __forceinline__ int bwd_xor(int r) {
-  if constexpr (RB >= 256) return r & 15;
-  else return (r / (256 / RB)) & (RB / 16 - 1);
+  if constexpr (RB >= 256) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else if constexpr (RB == 128) {
+    const int i = (r >> 1) & 7;
+    return ((i & 1) << 2) | (i >> 1);
+  } else {
+    return (r >> 2) & 3;
+  }
 }
 
 // Sum of lane l's and lane l ^ 32's values.
