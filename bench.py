@@ -168,7 +168,16 @@ def bwd_leg(fa, cfg, q, k, v, o, lse, stream, steps, warmup=10):
                         fa.fa_bwd_kernel_name(cfg.d, int(cfg.causal), 1)],
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                         "traffic": None}}
+                         "traffic": _bwd_traffic(cfg)}}
+
+
+def _bwd_traffic(cfg):
+    """HBM bytes of one fa_bwd call (both kernels) from the committed counter
+    summaries, or None (missing, or the sources changed since)."""
+    srcs = ["exact_attention_103_amd/csrc/fa_bwd.hip", "exact_attention_103_amd/csrc/fa_internal.h"]
+    tag = "causal" if cfg.causal else "nomask"
+    parts = [_traffic(f"fa_bwd_{k}_d{cfg.d}_{tag}", srcs) for k in ("dq", "dkdv")]
+    return None if any(x is None for x in parts) else sum(parts)
 
 
 def main():
