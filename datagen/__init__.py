@@ -36,6 +36,8 @@ __all__ = [
     "make_fwd_inputs",
     "make_decode_inputs",
     "make_bwd_inputs",
+    "make_serve_inputs",
+    "serve_config",
     "row_subset",
 ]
 
@@ -79,7 +81,7 @@ def gaussian_bf16(seed: int, shapes, input_scale: float = 1.0):
 
 @dataclass(frozen=True)
 class AttnConfig:
-    """One synthetic workload.  ``kind`` is "fwd" or "decode"."""
+    """One synthetic workload.  ``kind`` is "fwd", "decode" or "serve"."""
 
     name: str
     kind: str
@@ -93,6 +95,7 @@ class AttnConfig:
     seed: int
     input_scale: float = 1.0
     splits: tuple = field(default_factory=tuple)
+    min_len: int = 1            # serving decode: shortest per-sequence cache
 
     @property
     def scale(self) -> float:
@@ -115,6 +118,13 @@ def decode_config(name, B, Hq, Hkv, Nk, d, seed, splits=()):
                       tuple(splits))
 
 
+def serve_config(name, B, Hq, Hkv, Nq, Nk, d, causal, seed, min_len=1):
+    """Serving-shaped decode: Nq query rows per sequence, cache capacity Nk,
+    per-sequence lengths drawn uniformly from min_len..Nk."""
+    return AttnConfig(name, "serve", B, Hq, Hkv, Nq, Nk, d, causal, seed, 1.0, (),
+                      min_len)
+
+
 # The five workloads: a tiny non-causal case, a training-shape prefill (both
 # mask modes), a long-context causal prefill, a head-dim sweep and a GQA
 # split-KV decode over a 32k-token cache.
@@ -133,6 +143,9 @@ CONFIGS = {
                              input_scale=1 / math.sqrt(256)),
     "decode": decode_config("decode", 8, 32, 8, 32768, 128, seed=5,
                             splits=(16, 32, 64)),
+    # Serving-shaped decode (a NEXT row): 4 new tokens per sequence, causal
+    # among themselves, over per-sequence caches of 1k..32k tokens.
+    "serve": serve_config("serve", 8, 32, 8, 4, 32768, 128, True, seed=6, min_len=1024),
 }
 
 
@@ -152,6 +165,18 @@ def make_bwd_inputs(cfg: AttnConfig):
         [(cfg.B, cfg.Hq, cfg.Nq, cfg.d), (cfg.B, cfg.Hkv, cfg.Nk, cfg.d),
          (cfg.B, cfg.Hkv, cfg.Nk, cfg.d), (cfg.B, cfg.Hq, cfg.Nq, cfg.d)],
         cfg.input_scale)
+
+
+def make_serve_inputs(cfg: AttnConfig):
+    """bf16 bits for q [B][Hq][Nq][d], k_cache and v_cache [B][Hkv][Nk][d], and
+    int32 lengths [B] drawn from default_rng(seed + 1) in min_len..Nk."""
+    q, k, v = gaussian_bf16(
+        cfg.seed,
+        [(cfg.B, cfg.Hq, cfg.Nq, cfg.d), (cfg.B, cfg.Hkv, cfg.Nk, cfg.d),
+         (cfg.B, cfg.Hkv, cfg.Nk, cfg.d)],
+        cfg.input_scale)
+    lens = np.random.default_rng(cfg.seed + 1).integers(cfg.min_len, cfg.Nk + 1, size=cfg.B)
+    return q, k, v, lens.astype(np.int32)
 
 
 def make_decode_inputs(cfg: AttnConfig):

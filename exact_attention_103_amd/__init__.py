@@ -19,7 +19,9 @@ __all__ = [
     "fa_decode_num_splits", "fa_decode_max_splits", "fa_strerror",
     "fa_last_hip_error", "fa_fwd_kernel_name", "fa_decode_kernel_name",
     "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_kernel_name",
-    "fwd", "decode", "bwd", "EXPORTED_SYMBOLS", "LIB_PATH",
+    "fa_decode_serve", "fa_decode_serve_workspace_size", "fa_decode_serve_num_splits",
+    "fa_decode_serve_kernel_name",
+    "fwd", "decode", "decode_serve", "bwd", "EXPORTED_SYMBOLS", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -48,6 +50,11 @@ _SIGNATURES = {
                     _i, _vp, _sz, _vp]),
     "fa_bwd_workspace_size": (_sz, [_i, _i, _i]),
     "fa_bwd_kernel_name": (_cs, [_i, _i, _i]),
+    "fa_decode_serve": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i,
+                             _vp, _sz, _vp]),
+    "fa_decode_serve_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
+    "fa_decode_serve_num_splits": (_i, [_i, _i, _i, _i, _i, _i]),
+    "fa_decode_serve_kernel_name": (_cs, [_i, _i, _i, _i]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -100,6 +107,26 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale, caus
            workspace, workspace_bytes, stream=None):
     return lib().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale,
                         int(causal), workspace, workspace_bytes, stream)
+
+
+def fa_decode_serve(q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                    num_splits, workspace, workspace_bytes, stream=None):
+    return lib().fa_decode_serve(q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d,
+                                 scale, int(causal), num_splits, workspace, workspace_bytes,
+                                 stream)
+
+
+def fa_decode_serve_workspace_size(B, Hq, Nq, d, num_splits):
+    return lib().fa_decode_serve_workspace_size(B, Hq, Nq, d, num_splits)
+
+
+def fa_decode_serve_num_splits(B, Hq, Hkv, Nq, Nk, d):
+    return lib().fa_decode_serve_num_splits(B, Hq, Hkv, Nq, Nk, d)
+
+
+def fa_decode_serve_kernel_name(d, hq_per_kv, Nq, stage):
+    r = lib().fa_decode_serve_kernel_name(d, hq_per_kv, Nq, stage)
+    return r.decode() if r else None
 
 
 def fa_bwd_workspace_size(B, Hq, Nq):
@@ -246,3 +273,44 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, workspace=None):
     if rc != FA_OK:
         raise FAError(rc, "fa_bwd")
     return dq, dk, dv
+
+
+def decode_serve(q, k_cache, v_cache, seqlens=None, causal=False, scale=None, num_splits=0,
+                 out=None, lse=None, workspace=None):
+    """Serving-shaped decode: q [B][Hq][Nq][d] (Nq <= 16), caches
+    [B][Hkv][Nk][d] bf16 (Nk = capacity), seqlens int32 [B] device tensor or
+    None -> O [B][Hq][Nq][d], LSE [B][Hq][Nq]."""
+    import torch
+    _check_bf16("q", q, 4)
+    _check_bf16("k_cache", k_cache, 4)
+    _check_bf16("v_cache", v_cache, 4)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, Nk, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("caches must be [B][Hkv][Nk][d] with q's B and d")
+    sl = 0
+    if seqlens is not None:
+        if seqlens.dtype != torch.int32 or tuple(seqlens.shape) != (B,) or not seqlens.is_cuda:
+            raise ValueError("seqlens must be an int32 [B] device tensor")
+        sl = seqlens.contiguous().data_ptr()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    S = num_splits
+    if S == 0:
+        S = fa_decode_serve_num_splits(B, Hq, Hkv, Nq, Nk, d)
+        if S < 0:
+            raise FAError(S, "fa_decode_serve_num_splits")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    need = fa_decode_serve_workspace_size(B, Hq, Nq, d, S)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    rc = fa_decode_serve(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), sl or None,
+                         out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale),
+                         int(bool(causal)), S, workspace.data_ptr(), workspace.numel(),
+                         _stream_ptr())
+    if rc != FA_OK:
+        raise FAError(rc, "fa_decode_serve")
+    return out, lse

@@ -177,7 +177,97 @@ int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache, v
   p.splits = S;
   p.chunk = split_chunk(Nk, S);
   p.c = scale * fa::kLog2e;
+  p.seqlens = nullptr;
+  p.nq = 1;
+  p.causal = 0;
   const hipError_t e = fa::launch_decode(p, d, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : hip_fail(e);
+}
+
+size_t fa_decode_serve_workspace_size(int B, int Hq, int Nq, int d, int num_splits) {
+  if (!supported_d(d) || Nq < 1 || Nq > 16) return 0;
+  const int64_t n = checked_product({B, Hq, Nq, num_splits, d + 1, 4});
+  return n < 0 ? 0 : static_cast<size_t>(n);
+}
+
+int fa_decode_serve_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nk <= 0 || Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (Nq < 1 || Nq > 16) return FA_ERR_SHAPE;
+  if (!supported_d(d)) return FA_ERR_HEAD_DIM;
+  const int group = Hq / Hkv;
+  const int64_t per_split =
+      checked_product({B, Hkv, group / fa::decode_serve_group_tile(group, Nq)});
+  if (per_split < 0) return FA_ERR_TOO_LARGE;
+  int64_t s = (1024 + per_split - 1) / per_split;
+  const int64_t by_len = Nk / 256 > 0 ? Nk / 256 : 1;
+  if (s > by_len) s = by_len;
+  if (s > max_splits(Nk)) s = max_splits(Nk);
+  if (s < 1) s = 1;
+  return static_cast<int>(s);
+}
+
+int fa_decode_serve(const void* q, const void* k_cache, const void* v_cache, const int* seqlens,
+                    void* o, float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                    float scale, int causal, int num_splits, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !o || !lse) return FA_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nk <= 0) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0 || Nq < 1 || Nq > 16) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (!supported_d(d)) return FA_ERR_HEAD_DIM;
+  if (!scale_ok(scale)) return FA_ERR_SCALE;
+  if (num_splits < 0 || num_splits > max_splits(Nk)) return FA_ERR_SPLITS;
+  const int S = num_splits == 0 ? fa_decode_serve_num_splits(B, Hq, Hkv, Nq, Nk, d) : num_splits;
+  if (S < 0) return S;
+  const size_t need = fa_decode_serve_workspace_size(B, Hq, Nq, d, S);
+  if (need == 0) return FA_ERR_TOO_LARGE;
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+      !aligned16(lse) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0)
+    return FA_ERR_ALIGN;
+
+  const int group = Hq / Hkv;
+  const int64_t q_bytes = checked_product({B, Hq, Nq, d, 2});
+  const int64_t kv_bytes = checked_product({B, Hkv, Nk, d, 2});
+  const int64_t lse_bytes = checked_product({B, Hq, Nq, 4});
+  const int64_t grid = checked_product({B, Hkv, S, group / fa::decode_serve_group_tile(group, Nq)});
+  const int64_t grid2 = checked_product({B, Hq, Nq});
+  if (q_bytes < 0 || kv_bytes < 0 || lse_bytes < 0 || grid < 0 || grid > INT32_MAX ||
+      grid2 < 0 || grid2 > INT32_MAX)
+    return FA_ERR_TOO_LARGE;
+
+  const Span ins[4] = {span(q, q_bytes), span(k_cache, kv_bytes), span(v_cache, kv_bytes),
+                       span(seqlens, seqlens ? static_cast<int64_t>(B) * 4 : 0)};
+  const Span outs[3] = {span(o, q_bytes), span(lse, lse_bytes),
+                        span(workspace, static_cast<int64_t>(need))};
+  for (int i = 0; i < 3; ++i) {
+    for (const Span& in : ins)
+      if (overlaps(outs[i], in)) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], outs[j])) return FA_ERR_ALIAS;
+  }
+
+  fa::DecodeParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k_cache);
+  p.v = static_cast<const uint16_t*>(v_cache);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.o_part = static_cast<float*>(workspace);
+  p.lse_part = p.o_part + static_cast<size_t>(B) * Hq * Nq * S * d;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nk = Nk;
+  p.group = group;
+  p.splits = S;
+  p.chunk = split_chunk(Nk, S);
+  p.c = scale * fa::kLog2e;
+  p.seqlens = seqlens;
+  p.nq = Nq;
+  p.causal = causal;
+  const hipError_t e = fa::launch_decode_serve(p, d, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : hip_fail(e);
 }
 
@@ -275,6 +365,12 @@ const char* fa_fwd_kernel_name(int d, int causal, int Nq, int Nk) {
 
 const char* fa_decode_kernel_name(int d, int hq_per_kv, int stage) {
   return fa::decode_kernel_name(d, hq_per_kv, stage);
+}
+
+const char* fa_decode_serve_kernel_name(int d, int hq_per_kv, int Nq, int stage) {
+  if (stage == 1) return fa::decode_kernel_name(d, hq_per_kv, 1);
+  if (stage != 0) return nullptr;
+  return fa::decode_serve_kernel_name(d, hq_per_kv, Nq);
 }
 
 const char* fa_bwd_kernel_name(int d, int causal, int stage) {

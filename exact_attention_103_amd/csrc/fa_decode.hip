@@ -30,6 +30,7 @@
 
 #include "fa_internal.h"
 
+#include <limits.h>
 #include <math.h>
 
 namespace fa {
@@ -81,7 +82,13 @@ __device__ __forceinline__ float group4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int D, int GT>
+// SERVE = false: one query row per sequence, every sequence Nk keys.
+// SERVE = true (serving-shaped decode): Nq query rows per sequence and a
+// per-sequence key count seqlens[b] <= Nk (Nk is then the cache capacity, the
+// row stride of the K/V cache).  The MFMA columns are (query head, row)
+// pairs, GT * Nq <= 16 of them; with causal masking row i of sequence b sits
+// at position seqlens[b] - Nq + i and sees keys j <= that position.
+template <int D, int GT, bool SERVE>
 __device__ __forceinline__ void decode_split_body(const DecodeParams& p, lds_char* vs0,
                                                   lds_char* vs1, float* mlds) {
   using S = DecShape<D>;
@@ -89,8 +96,12 @@ __device__ __forceinline__ void decode_split_body(const DecodeParams& p, lds_cha
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int col = lane & 15;   // MFMA column: query head h0 + col
+  const int col = lane & 15;   // MFMA column: query head h0 + col (or a (head, row) pair)
   const int grp = lane >> 4;   // 16-lane group: k sub-block / row block
+  const int nq = SERVE ? p.nq : 1;
+  const int cols = GT * nq;                    // live MFMA columns
+  const int chd = SERVE ? col / nq : col;      // column -> query head within the tile
+  const int crow = SERVE ? col - chd * nq : 0; // column -> query row
 
   // Workgroup -> (b, kv head, split, head group); head group innermost so
   // workgroups that share K/V bytes run next to each other.
@@ -102,8 +113,16 @@ __device__ __forceinline__ void decode_split_body(const DecodeParams& p, lds_cha
   const int b = id / p.Hkv;
   const int h0 = kvh * p.group + hg * GT;   // first query head of this workgroup
 
-  const int kbeg = s * p.chunk;
-  const int kend = min(kbeg + p.chunk, p.Nk);
+  int len = p.Nk, chunk = p.chunk;
+  if (SERVE) {
+    if (p.seqlens) len = min(max(__builtin_amdgcn_readfirstlane(p.seqlens[b]), 0), p.Nk);
+    chunk = ((len + p.splits - 1) / p.splits + kDecodeChunkAlign - 1) / kDecodeChunkAlign *
+            kDecodeChunkAlign;
+  }
+  // Causal limit of this lane's column (SERVE only): keys j <= lim.
+  const int lim = (SERVE && p.causal) ? len - nq + crow : INT_MAX;
+  const int kbeg = s * chunk;
+  const int kend = min(kbeg + chunk, len);
   const int ntiles = kend > kbeg ? (kend - kbeg + kDecTile - 1) / kDecTile : 0;
   const int my = ntiles > wave ? (ntiles - wave + kDecWaves - 1) / kDecWaves : 0;
 
@@ -111,9 +130,10 @@ __device__ __forceinline__ void decode_split_body(const DecodeParams& p, lds_cha
   bf16x8 qf[S::KSTEPS];
 #pragma unroll
   for (int t = 0; t < S::KSTEPS; ++t) {
-    qf[t] = col < GT ? *reinterpret_cast<const bf16x8*>(
-                           p.q + ((size_t)(b * p.Hq + h0 + col)) * D + 32 * t + 8 * grp)
-                     : bf16x8{};
+    qf[t] = col < cols ? *reinterpret_cast<const bf16x8*>(
+                             p.q + ((size_t)(b * p.Hq + h0 + chd) * nq + crow) * D + 32 * t +
+                             8 * grp)
+                       : bf16x8{};
   }
 
   const size_t kvoff = ((size_t)(b * p.Hkv + kvh)) * p.Nk * D;
@@ -163,7 +183,9 @@ __device__ __forceinline__ void decode_split_body(const DecodeParams& p, lds_cha
     float sv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      sv[r] = (tb + 4 * grp + r < kend) ? sacc[r] * p.c : -INFINITY;
+      sv[r] = (tb + 4 * grp + r < kend && (!SERVE || tb + 4 * grp + r <= lim))
+                  ? sacc[r] * p.c
+                  : -INFINITY;
     const float mx = group4_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
     const float m_new = fmaxf(m, mx);
     if (__any(m_new > m + kDecRescaleThreshold)) {
@@ -218,8 +240,10 @@ __device__ __forceinline__ void decode_split_body(const DecodeParams& p, lds_cha
         make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
   __syncthreads();
 
-  for (int o = tid; o < GT * D; o += kDecThreads) {
+  for (int o = tid; o < cols * D; o += kDecThreads) {
     const int gq = o / D, dd = o % D;
+    const int gh = SERVE ? gq / nq : gq;
+    const int gr = SERVE ? gq - gh * nq : 0;
     float M = -1e30f;
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w) M = max_raw(M, sm_m[w * 16 + gq]);
@@ -230,7 +254,7 @@ __device__ __forceinline__ void decode_split_body(const DecodeParams& p, lds_cha
       W += wt * sm_l[w * 16 + gq];
       O += wt * sm_acc[((size_t)w * 16 + gq) * D + dd];
     }
-    const size_t ps = ((size_t)(b * p.Hq + h0 + gq)) * p.splits + s;
+    const size_t ps = ((size_t)(b * p.Hq + h0 + gh) * nq + gr) * p.splits + s;
     if (W > 0.f) {
       p.o_part[ps * D + dd] = O / W;
       if (dd == 0) p.lse_part[ps] = (M + log2f(W)) * kLn2;
@@ -279,7 +303,7 @@ __device__ __forceinline__ void decode_merge_body(const DecodeParams& p) {
   for (int s = tid & 63; s < S; s += 64) M = max_raw(M, lp[s]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = max_raw(M, __shfl_xor(M, off));
-  // M is finite: chunk 0 always holds at least one key.
+  // M is finite unless every chunk of the row is empty (Wt = 0 below).
 
   float O = 0.f, W = 0.f;
   for (int s0 = ph;;) {
@@ -303,23 +327,27 @@ __device__ __forceinline__ void decode_merge_body(const DecodeParams& p) {
       Ot += part[q * D + dd];
       Wt += red[q * D + dd];
     }
-    bf16x2 v = {(__bf16)(Ot / Wt), (__bf16)0.f};
+    // A row with no allowed key at all (only possible in the serving form)
+    // gets O = 0 and LSE = -inf.
+    bf16x2 v = {(__bf16)(Wt > 0.f ? Ot / Wt : 0.f), (__bf16)0.f};
     p.o[(size_t)bh * D + dd] = __builtin_bit_cast(unsigned, v) & 0xFFFFu;
-    if (dd == 0) p.lse[bh] = M + logf(Wt);
+    if (dd == 0) p.lse[bh] = Wt > 0.f ? M + logf(Wt) : -INFINITY;
   }
 }
 
 }  // namespace
 }  // namespace fa
 
-#define FA_DEC_SPLIT(D, GT)                                                              \
-  extern "C" __global__ void __launch_bounds__(fa::kDecThreads, 2)                       \
-      fa_decode_split_d##D##_g##GT(fa::DecodeParams p) {                                \
+#define FA_DEC_SPLIT_K(NAME, D, GT, SERVE)                                               \
+  extern "C" __global__ void __launch_bounds__(fa::kDecThreads, 2) NAME(fa::DecodeParams p) { \
     __shared__ __attribute__((aligned(1024))) char vs0[fa::kDecWaves * fa::DecShape<D>::VTILE]; \
     __shared__ __attribute__((aligned(1024))) char vs1[fa::kDecWaves * fa::DecShape<D>::VTILE]; \
     __shared__ __attribute__((aligned(16))) float mlds[fa::kDecWaves * 16 * (2 + D)];   \
-    fa::decode_split_body<D, GT>(p, (fa::lds_char*)vs0, (fa::lds_char*)vs1, mlds);      \
+    fa::decode_split_body<D, GT, SERVE>(p, (fa::lds_char*)vs0, (fa::lds_char*)vs1, mlds); \
   }
+#define FA_DEC_SPLIT(D, GT)                                          \
+  FA_DEC_SPLIT_K(fa_decode_split_d##D##_g##GT, D, GT, false)         \
+  FA_DEC_SPLIT_K(fa_decode_serve_split_d##D##_g##GT, D, GT, true)
 
 #define FA_DEC_MERGE(D)                                                               \
   extern "C" __global__ void __launch_bounds__(fa::kMergeThreads) fa_decode_merge_d##D( \
@@ -346,18 +374,29 @@ int decode_group_tile(int group) {
   return 1;
 }
 
+int decode_serve_group_tile(int group, int nq) {
+  for (int gt = 16; gt > 1; gt >>= 1)
+    if (group % gt == 0 && gt * nq <= 16) return gt;
+  return 1;
+}
+
 namespace {
 
-const void* split_fn(int d, int gt) {
-#define FA_CASE(D)                                                   \
-  case D:                                                            \
-    switch (gt) {                                                    \
-      case 1: return (const void*)fa_decode_split_d##D##_g1;         \
-      case 2: return (const void*)fa_decode_split_d##D##_g2;         \
-      case 4: return (const void*)fa_decode_split_d##D##_g4;         \
-      case 8: return (const void*)fa_decode_split_d##D##_g8;         \
-      case 16: return (const void*)fa_decode_split_d##D##_g16;       \
-    }                                                                \
+const void* split_fn(int d, int gt, bool serve) {
+#define FA_CASE(D)                                                                            \
+  case D:                                                                                     \
+    switch (gt) {                                                                             \
+      case 1: return serve ? (const void*)fa_decode_serve_split_d##D##_g1                     \
+                           : (const void*)fa_decode_split_d##D##_g1;                          \
+      case 2: return serve ? (const void*)fa_decode_serve_split_d##D##_g2                     \
+                           : (const void*)fa_decode_split_d##D##_g2;                          \
+      case 4: return serve ? (const void*)fa_decode_serve_split_d##D##_g4                     \
+                           : (const void*)fa_decode_split_d##D##_g4;                          \
+      case 8: return serve ? (const void*)fa_decode_serve_split_d##D##_g8                     \
+                           : (const void*)fa_decode_split_d##D##_g8;                          \
+      case 16: return serve ? (const void*)fa_decode_serve_split_d##D##_g16                   \
+                            : (const void*)fa_decode_split_d##D##_g16;                        \
+    }                                                                                         \
     return nullptr;
   switch (d) {
     FA_CASE(32)
@@ -409,9 +448,43 @@ const char* decode_kernel_name(int d, int group, int stage) {
   return split_names[di][gi];
 }
 
+const char* decode_serve_kernel_name(int d, int group, int nq) {
+  static const char* const names[4][5] = {
+      {"fa_decode_serve_split_d32_g1", "fa_decode_serve_split_d32_g2",
+       "fa_decode_serve_split_d32_g4", "fa_decode_serve_split_d32_g8",
+       "fa_decode_serve_split_d32_g16"},
+      {"fa_decode_serve_split_d64_g1", "fa_decode_serve_split_d64_g2",
+       "fa_decode_serve_split_d64_g4", "fa_decode_serve_split_d64_g8",
+       "fa_decode_serve_split_d64_g16"},
+      {"fa_decode_serve_split_d128_g1", "fa_decode_serve_split_d128_g2",
+       "fa_decode_serve_split_d128_g4", "fa_decode_serve_split_d128_g8",
+       "fa_decode_serve_split_d128_g16"},
+      {"fa_decode_serve_split_d256_g1", "fa_decode_serve_split_d256_g2",
+       "fa_decode_serve_split_d256_g4", "fa_decode_serve_split_d256_g8",
+       "fa_decode_serve_split_d256_g16"}};
+  const int di = d == 32 ? 0 : d == 64 ? 1 : d == 128 ? 2 : d == 256 ? 3 : -1;
+  if (di < 0 || group <= 0 || nq < 1 || nq > 16) return nullptr;
+  const int gt = decode_serve_group_tile(group, nq);
+  const int gi = gt == 1 ? 0 : gt == 2 ? 1 : gt == 4 ? 2 : gt == 8 ? 3 : 4;
+  return names[di][gi];
+}
+
+hipError_t launch_decode_serve(const DecodeParams& p, int d, hipStream_t s) {
+  const int gt = decode_serve_group_tile(p.group, p.nq);
+  const void* f1 = split_fn(d, gt, true);
+  const void* f2 = merge_fn(d);
+  if (!f1 || !f2) return hipErrorInvalidValue;
+  DecodeParams arg = p;
+  void* args[] = {&arg};
+  const unsigned n1 = (unsigned)(p.B * p.Hkv * p.splits * (p.group / gt));
+  hipError_t e = hipLaunchKernel(f1, dim3(n1), dim3(kDecThreads), args, 0, s);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel(f2, dim3((unsigned)(p.B * p.Hq * p.nq)), dim3(kMergeThreads), args, 0, s);
+}
+
 hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t s) {
   const int gt = decode_group_tile(p.group);
-  const void* f1 = split_fn(d, gt);
+  const void* f1 = split_fn(d, gt, false);
   const void* f2 = merge_fn(d);
   if (!f1 || !f2) return hipErrorInvalidValue;
   DecodeParams arg = p;

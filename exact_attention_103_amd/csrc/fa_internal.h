@@ -41,8 +41,15 @@ struct DecodeParams {
   int B, Hq, Hkv, Nk;
   int group;              // Hq / Hkv
   int splits;             // S
-  int chunk;              // keys per split (multiple of 64)
+  int chunk;              // keys per split (multiple of 64); per sequence when serving
   float c;                // scale * log2(e)
+  // Serving-shaped decode only (fa_decode_serve): Nq query rows per
+  // sequence (q, o, lse, o_part, lse_part gain an [Nq] axis after the head),
+  // per-sequence key counts seqlens[b] <= Nk (Nk = cache capacity; NULL = all
+  // Nk), and bottom-right causal masking among the Nq rows.
+  const int* seqlens;
+  int nq;
+  int causal;
 };
 
 // Arguments of one backward call (dQ kernel, then dK/dV kernel).  Tensors
@@ -68,6 +75,9 @@ struct BwdParams {
 // arguments were validated and return the hipError_t of the launch.
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t s);
+hipError_t launch_decode_serve(const DecodeParams& p, int d, hipStream_t s);
+const char* decode_serve_kernel_name(int d, int group, int nq);
+int decode_serve_group_tile(int group, int nq);
 const char* fwd_kernel_name(int d, bool causal, int Nq, int Nk);
 const char* decode_kernel_name(int d, int group, int stage);
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s);

@@ -5,7 +5,8 @@
 Prints one JSON line per workload: the kernel that ran, the median launch
 time (HIP events on the launch stream) and TFLOP/s for the forward (flop =
 4*B*H*Nq*Nk*d, halved when causal) or GB/s for the decode (K + V cache read
-once, plus q, O and LSE).  Inputs are random bf16 tensors of the workload's
+once, plus q, O and LSE; for the serving decode only each sequence's first
+seqlens[b] keys count).  Inputs are random bf16 tensors of the workload's
 shape and scaling; the forward's speed does not depend on the values.
 """
 
@@ -29,6 +30,8 @@ FWD = [  # name, B, H, N, d, causal, input scale
     ("sweep_d256", 2, 16, 4096, 256, True, 256 ** -0.5),
 ]
 DECODE = [(8, 32, 8, 32768, 128, s) for s in (0, 16, 32, 64)]
+SERVE = [(8, 32, 8, 4, 32768, 128, True, 6, S) for S in (0, 32, 64)] + \
+        [(8, 32, 8, 1, 32768, 128, False, 6, 0)]
 
 
 def _time(fn, iters, warmup, warm_ms=200.0):
@@ -93,6 +96,30 @@ def main():
                           "ms": round(ms, 4), "gbs": round(nbytes / ms / 1e6, 1),
                           "pct_of_8000": round(100 * nbytes / ms / 1e6 / 8000, 1)}), flush=True)
         del q, kc, vc, ws, o, lse
+    import numpy as np
+    for B, Hq, Hkv, Nq, Nk, d, causal, seed, S in SERVE:
+        # Per-sequence lengths as in the serving workload: uniform in 1024..Nk.
+        lens = np.random.default_rng(seed + 1).integers(1024, Nk + 1, size=B).astype(np.int32)
+        q = torch.randn(B, Hq, Nq, d, device="cuda").to(torch.bfloat16)
+        kc = torch.randn(B, Hkv, Nk, d, device="cuda").to(torch.bfloat16)
+        vc = torch.randn(B, Hkv, Nk, d, device="cuda").to(torch.bfloat16)
+        sl = torch.from_numpy(lens).to("cuda")
+        splits = S or fa.fa_decode_serve_num_splits(B, Hq, Hkv, Nq, Nk, d)
+        ws = torch.empty(fa.fa_decode_serve_workspace_size(B, Hq, Nq, d, splits),
+                         dtype=torch.uint8, device="cuda")
+        o = torch.empty_like(q)
+        lse = torch.empty(B, Hq, Nq, device="cuda", dtype=torch.float32)
+        ms = _time(lambda: fa.decode_serve(q, kc, vc, sl, causal=causal, num_splits=splits,
+                                           out=o, lse=lse, workspace=ws), args.iters, args.warmup)
+        nbytes = 2 * Hkv * int(lens.sum()) * d * 2 + 2 * B * Hq * Nq * d * 2 + 4 * B * Hq * Nq
+        print(json.dumps({"workload": "serve", "B": B, "Hq": Hq, "Hkv": Hkv, "Nq": Nq, "Nk": Nk,
+                          "d": d, "causal": causal, "mean_len": float(lens.mean()),
+                          "splits": splits,
+                          "kernels": [fa.fa_decode_serve_kernel_name(d, Hq // Hkv, Nq, 0),
+                                      fa.fa_decode_serve_kernel_name(d, Hq // Hkv, Nq, 1)],
+                          "ms": round(ms, 4), "gbs": round(nbytes / ms / 1e6, 1),
+                          "pct_of_8000": round(100 * nbytes / ms / 1e6 / 8000, 1)}), flush=True)
+        del q, kc, vc, ws, o, lse, sl
 
 
 if __name__ == "__main__":

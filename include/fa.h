@@ -38,7 +38,8 @@ extern "C" {
 enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = -1,       /* a required pointer is NULL                      */
-  FA_ERR_SHAPE = -2,      /* B, H or N <= 0, Hq % Hkv != 0, causal && Nq > Nk */
+  FA_ERR_SHAPE = -2,      /* B, H or N <= 0, Hq % Hkv != 0, causal && Nq > Nk,
+                             serving decode Nq outside 1..16                 */
   FA_ERR_HEAD_DIM = -3,   /* d not in {32, 64, 128, 256} ({32, 64, 128} bwd) */
   FA_ERR_ALIGN = -4,      /* a tensor pointer is not 16-byte aligned         */
   FA_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required         */
@@ -109,6 +110,45 @@ int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                       int d, float scale, int num_splits, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/*
+ * fa_decode_serve -- serving-shaped split-KV decode: Nq (1..16) query rows
+ * per sequence and a per-sequence KV length, over a padded cache.
+ *
+ * The same split/merge method as fa_decode_splitkv ([Evolution] §6) for
+ * the decode step of a serving engine, where each sequence of a batch has
+ * its own cache length (tens of thousands of tokens, [Evolution] §6) and a
+ * step may score several new tokens at once.  For sequence b with n_b =
+ * seqlens[b] keys (clamped to 0..Nk; seqlens NULL means n_b = Nk for all b),
+ * query row i attends to keys j < n_b, and with causal = 1 only to
+ * j <= n_b - Nq + i (the rows are the last Nq positions of the sequence).
+ * Each sequence's keys are cut into num_splits chunks of
+ * ceil(n_b / num_splits) keys rounded up to a multiple of 64; chunks past
+ * n_b are empty and get weight 0.  A row with no allowed key (n_b = 0, or
+ * causal rows with n_b - Nq + i < 0) gets O = 0 and LSE = -inf.
+ *
+ *   q         bf16 [B][Hq][Nq][d]
+ *   k_cache   bf16 [B][Hkv][Nk][d]   (Nk = capacity; rows >= n_b are not read)
+ *   v_cache   bf16 [B][Hkv][Nk][d]
+ *   seqlens   int32 [B] device array, 4-byte aligned, or NULL
+ *   o         bf16 [B][Hq][Nq][d]    output
+ *   lse       fp32 [B][Hq][Nq]       output, natural log
+ *   num_splits 0 = fa_decode_serve_num_splits(...), else 1 .. fa_decode_max_splits(Nk)
+ *   workspace at least fa_decode_serve_workspace_size(B, Hq, Nq, d, splits)
+ *             bytes, 16-byte aligned, caller-owned, overlapping no tensor.
+ */
+int fa_decode_serve(const void* q, const void* k_cache, const void* v_cache,
+                    const int* seqlens, void* o, float* lse, int B, int Hq, int Hkv,
+                    int Nq, int Nk, int d, float scale, int causal, int num_splits,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of serving-decode workspace: 4*B*Hq*Nq*S*(d+1).  0 on invalid sizes. */
+size_t fa_decode_serve_workspace_size(int B, int Hq, int Nq, int d, int num_splits);
+
+/* Split count used by fa_decode_serve when num_splits == 0 (as
+ * fa_decode_num_splits, for the workgroups the Nq rows need); negative
+ * fa_status for invalid sizes. */
+int fa_decode_serve_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+
 /* Bytes of decode workspace: fp32 partial outputs [B][Hq][S][d] followed by
  * fp32 partial LSEs [B][Hq][S], i.e. 4*B*Hq*S*(d+1).  0 on invalid sizes. */
 size_t fa_decode_workspace_size(int B, int Hq, int d, int num_splits);
@@ -177,6 +217,9 @@ const char* fa_decode_kernel_name(int d, int hq_per_kv, int stage);
 /* fa_bwd_kernel_name: stage 0 = dQ kernel (also writes Delta), stage 1 =
  * dK/dV kernel. */
 const char* fa_bwd_kernel_name(int d, int causal, int stage);
+/* fa_decode_serve_kernel_name: stage 0 = split kernel (depends on the query
+ * heads per KV head and on Nq), stage 1 = merge kernel. */
+const char* fa_decode_serve_kernel_name(int d, int hq_per_kv, int Nq, int stage);
 
 #ifdef __cplusplus
 }

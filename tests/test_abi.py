@@ -95,6 +95,24 @@ def test_bwd_kernel_names_and_workspace():
     assert fa.fa_bwd_workspace_size(0, 4, 100) == 0
 
 
+def test_serve_helpers():
+    assert fa.fa_decode_serve_workspace_size(2, 8, 4, 128, 3) == 4 * 2 * 8 * 4 * 3 * 129
+    assert fa.fa_decode_serve_workspace_size(2, 8, 17, 128, 3) == 0
+    assert fa.fa_decode_serve_workspace_size(2, 8, 4, 100, 3) == 0
+    # group 4 with 4 rows: 4 heads x 4 rows = 16 MFMA columns per workgroup
+    assert fa.fa_decode_serve_kernel_name(128, 4, 4, 0) == "fa_decode_serve_split_d128_g4"
+    assert fa.fa_decode_serve_kernel_name(128, 4, 5, 0) == "fa_decode_serve_split_d128_g2"
+    assert fa.fa_decode_serve_kernel_name(128, 16, 1, 0) == "fa_decode_serve_split_d128_g16"
+    assert fa.fa_decode_serve_kernel_name(128, 16, 16, 0) == "fa_decode_serve_split_d128_g1"
+    assert fa.fa_decode_serve_kernel_name(128, 4, 4, 1) == "fa_decode_merge_d128"
+    assert fa.fa_decode_serve_kernel_name(128, 4, 17, 0) is None
+    assert fa.fa_decode_serve_kernel_name(96, 4, 4, 0) is None
+    s = fa.fa_decode_serve_num_splits(8, 32, 8, 4, 32768, 128)
+    assert 1 <= s <= fa.fa_decode_max_splits(32768)
+    assert fa.fa_decode_serve_num_splits(8, 32, 8, 0, 32768, 128) == -2
+    assert fa.fa_decode_serve_num_splits(8, 32, 8, 17, 32768, 128) == -2
+
+
 def test_workspace_and_splits():
     assert fa.fa_decode_workspace_size(8, 32, 128, 32) == 4 * 8 * 32 * 32 * 129
     assert fa.fa_decode_workspace_size(8, 32, 100, 32) == 0
@@ -211,3 +229,32 @@ def _bwd(**kw):
 ])
 def test_bwd_rejects(kw, code):
     assert _bwd(**kw) == code
+
+
+SQ, SK, SV, SL, SO, SLSE, SW = (0x40000000 + 0x1000000 * i for i in range(7))
+GOOD_SERVE = dict(q=SQ, k=SK, v=SV, sl=SL, o=SO, lse=SLSE, B=2, Hq=8, Hkv=2, Nq=4, Nk=1000,
+                  d=128, scale=0.088, causal=1, S=4, ws=SW, ws_bytes=1 << 22)
+
+
+def _serve(**kw):
+    a = dict(GOOD_SERVE)
+    a.update(kw)
+    return fa.fa_decode_serve(a["q"], a["k"], a["v"], a["sl"], a["o"], a["lse"], a["B"], a["Hq"],
+                              a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], a["S"],
+                              a["ws"], a["ws_bytes"], None)
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), -1), (dict(k=0), -1), (dict(v=0), -1), (dict(o=0), -1), (dict(lse=0), -1),
+    (dict(B=0), -2), (dict(Hq=6, Hkv=4), -2), (dict(Nq=0), -2), (dict(Nq=17), -2),
+    (dict(Nk=0), -2), (dict(causal=3), -2),
+    (dict(d=96), -3),
+    (dict(sl=SL + 2), -4), (dict(q=SQ + 8), -4), (dict(ws=SW + 4), -4),
+    (dict(ws=0), -5), (dict(ws_bytes=4 * 2 * 8 * 4 * 4 * 129 - 1), -5),
+    (dict(S=-1), -6), (dict(S=17), -6),
+    (dict(scale=0.0), -8),
+    (dict(o=SQ), -9), (dict(ws=SL), -9), (dict(lse=SV + 64), -9), (dict(o=SW), -9),
+])
+def test_serve_rejects(kw, code):
+    assert _serve(**kw) == code
