@@ -115,9 +115,10 @@ int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
  * per sequence and a per-sequence KV length, over a padded cache.
  *
  * The same split/merge method as fa_decode_splitkv ([Evolution] §6) for
- * the decode step of a serving engine, where each sequence of a batch has
- * its own cache length (tens of thousands of tokens, [Evolution] §6) and a
- * step may score several new tokens at once.  For sequence b with n_b =
+ * the decode step of a serving engine ([Evolution] §7 compares one), where
+ * each sequence of a batch has its own cache length (up to tens of
+ * thousands of tokens, [Evolution] §6) and a step may score several new
+ * tokens at once.  For sequence b with n_b =
  * seqlens[b] keys (clamped to 0..Nk; seqlens NULL means n_b = Nk for all b),
  * query row i attends to keys j < n_b, and with causal = 1 only to
  * j <= n_b - Nq + i (the rows are the last Nq positions of the sequence).
