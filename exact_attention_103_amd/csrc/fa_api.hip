@@ -299,7 +299,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   const int64_t kv_bytes = checked_product({B, Hkv, Nk, d, 2});
   const int64_t lse_bytes = checked_product({B, Hq, Nq, 4});
   const int64_t g1 = checked_product({(Nq + 127) / 128, B, Hq});
-  const int64_t g2 = checked_product({(Nk + 127) / 128, B, Hkv});
+  const int64_t g2 = checked_product({(Nk + 63) / 64, B, Hkv});
   if (q_bytes < 0 || kv_bytes < 0 || lse_bytes < 0 || g1 < 0 || g1 > INT32_MAX || g2 < 0 ||
       g2 > INT32_MAX)
     return FA_ERR_TOO_LARGE;

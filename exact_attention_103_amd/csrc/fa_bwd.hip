@@ -53,10 +53,23 @@ typedef __attribute__((address_space(3))) char lds_char;
 // For 256-byte rows X swaps the two 2-bit digits of r mod 16; for 128-byte
 // rows (two per line) it does the same on the row's line index; 64-byte rows
 // fill a line with four different rows and need only the first property.
-template <int RB>
+//
+// The dK/dV kernel reads its tiles with the 16x16x32 operand shapes: 16
+// rows per 16-lane group for the row-major reads, 2 chunks of 4 rows per
+// group for the transposing reads.  Measured with rocprofv3 on gfx950
+// (SQ_LDS_BANK_CONFLICT, one probe kernel per pattern and swizzle), X = i
+// (the row index i within the bank-line period) is conflict-free for the
+// first pattern only, the digit swap and rotations for the second only, and
+// SW = 1, X = i ^ (i << 1), for both.
+template <int RB, int SW = 0>
 __device__ __forceinline__ int bwd_xor(int r) {
-  if constexpr (RB >= 256) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else if constexpr (RB == 128) {
+  if constexpr (SW == 1) {
+    constexpr int mask = RB >= 256 ? 15 : RB == 128 ? 7 : 3;
+    const int i = (r / (RB >= 256 ? 1 : 256 / RB)) & mask;
+    return (i ^ (i << 1)) & mask;
+  } else if constexpr (RB >= 256) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  } else if constexpr (RB == 128) {
     const int i = (r >> 1) & 7;
     return ((i & 1) << 2) | (i >> 1);
   } else {
@@ -81,27 +94,27 @@ struct BwdShape {
 constexpr int kBwdWaves = 4;
 constexpr int kDqRows = 32 * kBwdWaves;    // query rows per dQ workgroup
 constexpr int kDqKeys = 64;                // keys per K/V tile in the dQ kernel
-constexpr int kDkvKeys = 32 * kBwdWaves;   // keys per dK/dV workgroup
+constexpr int kDkvKeys = 16 * kBwdWaves;   // keys per dK/dV workgroup (16 per wave)
 constexpr int kDkvRows = 32;               // query rows per Q/dO tile in the dK/dV kernel
 
 // Direct global -> LDS copy of ROWS rows (from row r0, rows past nrows re-read
 // row nrows-1) of a row-major [.][D] bf16 matrix, swizzled with bwd_xor.
 // Wave load i writes 1 KB block i*NW + wave of the tile; lane l of it fetches
 // the global chunk whose swizzled position is that block's l-th chunk.
-template <int D, int ROWS>
+template <int D, int ROWS, int SW = 0, int NW = kBwdWaves>
 __device__ __forceinline__ void dma_rows(const uint16_t* base, int r0, int nrows, lds_char* tile,
                                          int wave, int lane) {
   constexpr int CPR = D / 8;
   constexpr int BLKS = ROWS * CPR / 64;
-  constexpr int LOADS = (BLKS + kBwdWaves - 1) / kBwdWaves;
+  constexpr int LOADS = (BLKS + NW - 1) / NW;
   static_assert((ROWS * CPR) % 64 == 0, "whole 1 KB blocks");
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int blk = i * kBwdWaves + wave;   // uniform across the wave
-    if (BLKS % kBwdWaves != 0 && blk >= BLKS) break;
+    const int blk = i * NW + wave;   // uniform across the wave
+    if (BLKS % NW != 0 && blk >= BLKS) break;
     const int P = blk * 64 + lane;
     const int row = P / CPR;
-    const int c = (P % CPR) ^ bwd_xor<2 * D>(row);
+    const int c = (P % CPR) ^ bwd_xor<2 * D, SW>(row);
     const int r = min(r0 + row, nrows - 1);
     __builtin_amdgcn_global_load_lds(base + (size_t)r * D + c * 8, tile + blk * 1024, 16, 0, 0);
   }
@@ -139,9 +152,10 @@ __device__ __forceinline__ bf16x8 tr_read(const lds_char* t, int lo_off, int hi_
 }
 
 // Row-major MFMA A operand: 8 bf16 of row r, logical chunk c, of a bwd tile.
-template <int RB>
+template <int RB, int SW = 0>
 __device__ __forceinline__ bf16x8 row_read(const lds_char* t, int r, int c) {
-  return *(const __attribute__((address_space(3))) bf16x8*)(t + r * RB + ((c ^ bwd_xor<RB>(r)) << 4));
+  return *(const __attribute__((address_space(3))) bf16x8*)(t + r * RB +
+                                                            ((c ^ bwd_xor<RB, SW>(r)) << 4));
 }
 
 // ---------------------------------------------------------------------------
@@ -288,28 +302,33 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, lds_char* kb0, l
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
-// LDS: the workgroup's K block (kDkvKeys rows, read as MFMA B operands) and,
-// per stage, a Q tile, a dO tile (kDkvRows rows each) and the LSE and Delta
-// of those rows (fp32).
+// Each wave owns 16 keys and works with 16x16x32 MFMAs, which keeps its
+// state small: K^T and V^T of its keys as B operands (D/4 registers each)
+// and the dK^T, dV^T accumulators (D/2 registers each).  LDS per stage: a Q
+// tile and a dO tile (kDkvRows rows each, swizzle SW = 1), then the LSE and
+// Delta of those rows (fp32).
+constexpr int kDkvWaves = 4;
+
 template <int D>
 struct DkvStage {
-  static constexpr int KBLOCK = kDkvKeys * 2 * D;
   static constexpr int TILE = kDkvRows * 2 * D;
   static constexpr int STATS = 2 * kDkvRows * 4;
 };
 
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* kblock,
-                                              lds_char* qt0, lds_char* qt1, lds_char* dt0,
-                                              lds_char* dt1, lds_char* st0, lds_char* st1) {
+__device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* qt0, lds_char* qt1,
+                                              lds_char* dt0, lds_char* dt1, lds_char* st0,
+                                              lds_char* st1) {
   using S = BwdShape<D>;
-  constexpr int BM = kDkvRows, BNK = kDkvKeys;
-  static_assert(BM == 32, "one 32-row block per stage");
+  constexpr int BM = kDkvRows, BNK = kDkvKeys, NW = kDkvWaves;
+  constexpr int KT = D / 32;   // 16x16x32 k-steps over d
+  constexpr int DB = D / 16;   // 16-row d blocks of dK^T, dV^T
+  static_assert(BM == 32 && BNK == 16 * NW, "two 16-row blocks per tile, 16 keys per wave");
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int hl = lane >> 5;
-  const int n = lane & 31;
+  const int n = lane & 15;     // MFMA column: key kw0 + n
+  const int grp = lane >> 4;   // 16-lane group
 
   const int BG = p.B * p.Hkv;
   const int bg = blockIdx.x % BG;
@@ -317,20 +336,19 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* kblo
   const int b = bg / p.Hkv;
   const int g = bg - b * p.Hkv;
   const int k0 = kblk * BNK;
-  const int kw0 = k0 + 32 * wave;                 // first key of this wave
+  const int kw0 = k0 + 16 * wave;                 // first key of this wave
   const int key = kw0 + n;
   const int off = p.Nk - p.Nq;
   const bool live = key < p.Nk;
-  const uint16_t* kbase = p.k + (size_t)bg * p.Nk * D;
   const size_t kvrow = ((size_t)bg * p.Nk + key) * D;
 
-  // V^T of this lane's key as MFMA B operands (d = 16t + 8hl .. +7); K^T is
-  // read from the K block in LDS with the same layout (rows 32*wave + n).
-  bf16x8 vf[S::KSTEPS];
+  // K^T and V^T of this lane's key as B operands: d = 32t + 8grp .. +7.
+  bf16x8 kf[KT], vf[KT];
 #pragma unroll
-  for (int t = 0; t < S::KSTEPS; ++t)
-    vf[t] = live ? *reinterpret_cast<const bf16x8*>(p.v + kvrow + 16 * t + 8 * hl) : bf16x8{};
-  dma_rows<D, BNK>(kbase, k0, p.Nk, kblock, wave, lane);
+  for (int t = 0; t < KT; ++t) {
+    kf[t] = live ? *reinterpret_cast<const bf16x8*>(p.k + kvrow + 32 * t + 8 * grp) : bf16x8{};
+    vf[t] = live ? *reinterpret_cast<const bf16x8*>(p.v + kvrow + 32 * t + 8 * grp) : bf16x8{};
+  }
 
   // Query tiles: every query head of the group, rows from the first one that
   // sees key k0 (causal) to Nq.
@@ -338,22 +356,33 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* kblo
   const int nqt = (p.Nq - qstart + BM - 1) / BM;
   const int steps = p.group * nqt;
 
-  int toff[2][S::DB];
-  tr_offsets<D>(lane, toff);
-
-  f32x16 dk[S::DB], dv[S::DB];
+  // Transposing reads of a 16-wide d block db: lane (grp, n) addresses row
+  // 4grp + n/4 (+16 for the second row block), columns 16db + 4(n%4) .. +3,
+  // and receives rows 4grp + 0..3 of column 16db + n: the queries that the
+  // B-operand registers 0..3 (4..7) of its column hold.
+  int toff[DB];
+  {
+    const int r = 4 * grp + (n >> 2);
 #pragma unroll
-  for (int db = 0; db < S::DB; ++db) {
-    dk[db] = f32x16{};
-    dv[db] = f32x16{};
+    for (int db = 0; db < DB; ++db) {
+      const int c = 2 * db + ((n & 3) >> 1);
+      toff[db] = r * S::RB + ((c ^ bwd_xor<S::RB, 1>(r)) << 4) + 8 * (n & 1);
+    }
+  }
+
+  f32x4 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dk[db] = f32x4{};
+    dv[db] = f32x4{};
   }
 
   auto tile_row = [&](int s) { return qstart + (s % nqt) * BM; };
   auto load = [&](int s, lds_char* qt, lds_char* dt, lds_char* st) {
     const int h = g * p.group + s / nqt, i0 = tile_row(s);
     const size_t hb = (size_t)(b * p.Hq + h) * p.Nq;
-    dma_rows<D, BM>(p.q + hb * D, i0, p.Nq, qt, wave, lane);
-    dma_rows<D, BM>(p.dout + hb * D, i0, p.Nq, dt, wave, lane);
+    dma_rows<D, BM, 1, NW>(p.q + hb * D, i0, p.Nq, qt, wave, lane);
+    dma_rows<D, BM, 1, NW>(p.dout + hb * D, i0, p.Nq, dt, wave, lane);
     if (wave == 0) {   // lanes 0-31: LSE of the BM rows, lanes 32-63: Delta
       const float* src = (lane < BM ? p.lse : p.delta - BM) + hb;
       __builtin_amdgcn_global_load_lds(src + min(i0 + (lane & (BM - 1)), p.Nq - 1) + (lane & BM),
@@ -365,60 +394,57 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* kblo
                   lds_char* dw, lds_char* sw, int s) {
     if (s + 1 < steps) load(s + 1, qw, dw, sw);
     const int i0 = tile_row(s);
-    const __attribute__((address_space(3))) float* lse_t =
-        (const __attribute__((address_space(3))) float*)st;
-    const __attribute__((address_space(3))) float* del_t = lse_t + BM;
+    const __attribute__((address_space(3))) f32x4* lse4 =
+        (const __attribute__((address_space(3))) f32x4*)st;
+    const __attribute__((address_space(3))) f32x4* del4 = lse4 + BM / 4;
 
-    // S = Q K^T: one key per lane, rows 8(r/4) + 4hl + r%4 of the tile.
-    f32x16 sacc = f32x16{};
+    // S = Q K^T and dP = dO V^T for the two 16-row blocks: lane (grp, n)
+    // gets rows 16qb + 4grp + r (r = 0..3) of key n.
+    f32x4 sacc[2], dpacc[2];
 #pragma unroll
-    for (int t = 0; t < S::KSTEPS; ++t)
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<S::RB>(qt, n, 2 * t + hl),
-                                                     row_read<S::RB>(kblock, 32 * wave + n, 2 * t + hl),
-                                                     sacc, 0, 0, 0);
-    if ((i0 + 31 >= p.Nq) || (CAUSAL && kw0 + 31 > i0 + off)) {
+    for (int qb = 0; qb < 2; ++qb) {
+      sacc[qb] = f32x4{};
+      dpacc[qb] = f32x4{};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ri = i0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        if (ri >= p.Nq || (CAUSAL && key > ri + off)) sacc[r] = -INFINITY;
+      for (int t = 0; t < KT; ++t) {
+        sacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            row_read<S::RB, 1>(qt, 16 * qb + n, 4 * t + grp), kf[t], sacc[qb], 0, 0, 0);
+        dpacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            row_read<S::RB, 1>(dt, 16 * qb + n, 4 * t + grp), vf[t], dpacc[qb], 0, 0, 0);
       }
     }
-    // P = exp(S - LSE) in base 2, rounded to bf16: the B operand of
-    // dV^T += dO^T P, and the P of dS below.
-    bf16x8 pb[2];
+    if ((i0 + 31 >= p.Nq) || (CAUSAL && kw0 + 15 > i0 + off)) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float l = lse_t[8 * (r >> 2) + 4 * hl + (r & 3)];
-      pb[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[r], p.c, -l * kLog2e));
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ri = i0 + 16 * qb + 4 * grp + r;
+          if (ri >= p.Nq || (CAUSAL && key > ri + off)) sacc[qb][r] = -INFINITY;
+        }
     }
+    // P = exp(S - LSE) (base 2) and dS = P (dP - Delta), as bf16 B operands;
+    // register 4qb + r holds row 16qb + 4grp + r.
+    bf16x8 pb, sb;
 #pragma unroll
-    for (int kq = 0; kq < 2; ++kq)
+    for (int qb = 0; qb < 2; ++qb) {
+      const f32x4 l4 = lse4[4 * qb + grp];
+      const f32x4 d4 = del4[4 * qb + grp];
 #pragma unroll
-      for (int db = 0; db < S::DB; ++db) {
-        const int ro = 16 * kq * S::RB;
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            tr_read(dt, toff[0][db] + ro, toff[1][db] + ro), pb[kq], dv[db], 0, 0, 0);
+      for (int r = 0; r < 4; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[qb][r], p.c, -l4[r] * kLog2e));
+        pb[4 * qb + r] = (__bf16)pr;
+        sb[4 * qb + r] = (__bf16)(pr * (dpacc[qb][r] - d4[r]));
       }
-    // dP = dO V^T, then dS = P (dP - Delta) as the B operand of dK^T += Q^T dS.
-    f32x16 dpacc = f32x16{};
-#pragma unroll
-    for (int t = 0; t < S::KSTEPS; ++t)
-      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<S::RB>(dt, n, 2 * t + hl), vf[t],
-                                                      dpacc, 0, 0, 0);
-    bf16x8 sb[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float dl = del_t[8 * (r >> 2) + 4 * hl + (r & 3)];
-      sb[r >> 3][r & 7] = (__bf16)((float)pb[r >> 3][r & 7] * (dpacc[r] - dl));
     }
+    // dV^T += dO^T P and dK^T += Q^T dS, the transposed A operands read from
+    // the dO and Q tiles.
 #pragma unroll
-    for (int kq = 0; kq < 2; ++kq)
-#pragma unroll
-      for (int db = 0; db < S::DB; ++db) {
-        const int ro = 16 * kq * S::RB;
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            tr_read(qt, toff[0][db] + ro, toff[1][db] + ro), sb[kq], dk[db], 0, 0, 0);
-      }
+    for (int db = 0; db < DB; ++db) {
+      dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          tr_read(dt, toff[db], toff[db] + 16 * S::RB), pb, dv[db], 0, 0, 0);
+      dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          tr_read(qt, toff[db], toff[db] + 16 * S::RB), sb, dk[db], 0, 0, 0);
+    }
     __syncthreads();
   };
 
@@ -429,25 +455,23 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* kblo
     if (s + 1 < steps) step(qt1, dt1, st1, qt0, dt0, st0, s + 1);
   }
 
-  // dK = scale * acc, dV = acc, bf16; lane holds d rows 32db + 8(r/4) + 4hl
-  // + r%4 of its key.
+  // dK = scale * acc, dV = acc, bf16; lane (grp, n) holds d rows 16db +
+  // 4grp + r of key n.
   if (live) {
 #pragma unroll
-    for (int db = 0; db < S::DB; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        bf16x2 klo = {(__bf16)(dk[db][4 * r4 + 0] * p.scale), (__bf16)(dk[db][4 * r4 + 1] * p.scale)};
-        bf16x2 khi = {(__bf16)(dk[db][4 * r4 + 2] * p.scale), (__bf16)(dk[db][4 * r4 + 3] * p.scale)};
-        bf16x2 vlo = {(__bf16)dv[db][4 * r4 + 0], (__bf16)dv[db][4 * r4 + 1]};
-        bf16x2 vhi = {(__bf16)dv[db][4 * r4 + 2], (__bf16)dv[db][4 * r4 + 3]};
-        uint2 wk, wv;
-        wk.x = __builtin_bit_cast(unsigned, klo);
-        wk.y = __builtin_bit_cast(unsigned, khi);
-        wv.x = __builtin_bit_cast(unsigned, vlo);
-        wv.y = __builtin_bit_cast(unsigned, vhi);
-        *reinterpret_cast<uint2*>(p.dk + kvrow + 32 * db + 8 * r4 + 4 * hl) = wk;
-        *reinterpret_cast<uint2*>(p.dv + kvrow + 32 * db + 8 * r4 + 4 * hl) = wv;
-      }
+    for (int db = 0; db < DB; ++db) {
+      bf16x2 klo = {(__bf16)(dk[db][0] * p.scale), (__bf16)(dk[db][1] * p.scale)};
+      bf16x2 khi = {(__bf16)(dk[db][2] * p.scale), (__bf16)(dk[db][3] * p.scale)};
+      bf16x2 vlo = {(__bf16)dv[db][0], (__bf16)dv[db][1]};
+      bf16x2 vhi = {(__bf16)dv[db][2], (__bf16)dv[db][3]};
+      uint2 wk, wv;
+      wk.x = __builtin_bit_cast(unsigned, klo);
+      wk.y = __builtin_bit_cast(unsigned, khi);
+      wv.x = __builtin_bit_cast(unsigned, vlo);
+      wv.y = __builtin_bit_cast(unsigned, vhi);
+      *reinterpret_cast<uint2*>(p.dk + kvrow + 16 * db + 4 * grp) = wk;
+      *reinterpret_cast<uint2*>(p.dv + kvrow + 16 * db + 4 * grp) = wv;
+    }
   }
 }
 
@@ -466,16 +490,15 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* kblo
   }
 
 #define FA_BWD_DKDV(D, CAUSAL, NAME)                                                       \
-  extern "C" __global__ void __launch_bounds__(64 * fa::kBwdWaves, 2) NAME(fa::BwdParams p) { \
+  extern "C" __global__ void __launch_bounds__(64 * fa::kDkvWaves, 3) NAME(fa::BwdParams p) { \
     using St = fa::DkvStage<D>;                                                            \
-    __shared__ __attribute__((aligned(1024))) char kb[St::KBLOCK];                         \
     __shared__ __attribute__((aligned(1024))) char q0[St::TILE];                           \
     __shared__ __attribute__((aligned(1024))) char q1[St::TILE];                           \
     __shared__ __attribute__((aligned(1024))) char d0[St::TILE];                           \
     __shared__ __attribute__((aligned(1024))) char d1[St::TILE];                           \
     __shared__ __attribute__((aligned(256))) char s0[St::STATS];                           \
     __shared__ __attribute__((aligned(256))) char s1[St::STATS];                           \
-    fa::bwd_dkdv_body<D, CAUSAL>(p, (fa::lds_char*)kb, (fa::lds_char*)q0, (fa::lds_char*)q1, \
+    fa::bwd_dkdv_body<D, CAUSAL>(p, (fa::lds_char*)q0, (fa::lds_char*)q1,                  \
                                  (fa::lds_char*)d0, (fa::lds_char*)d1,                     \
                                  (fa::lds_char*)s0, (fa::lds_char*)s1);                    \
   }
