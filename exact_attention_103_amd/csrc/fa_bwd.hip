@@ -21,12 +21,12 @@
 //                  K/V tiles of its KV head through LDS and accumulates dQ in
 //                  registers (S^T, dP^T and dQ^T as in the forward: one query
 //                  per lane).
-//   fa_bwd_dkdv_*  one workgroup of 4 waves per (128-key block, batch*KV
-//                  head).  Each wave owns 32 keys: their V stays in registers
-//                  and their K in an LDS block, both read as MFMA B operands;
-//                  the wave streams 32-row Q/dO tiles of every query head of
-//                  the group and accumulates dK and dV (S, dP with one key per
-//                  lane; dV^T, dK^T).  Two waves per SIMD.
+//   fa_bwd_dkdv_*  one workgroup of 4 waves per (64-key block, batch*KV
+//                  head).  Each wave owns 16 keys whose K and V stay in
+//                  registers as the B operands of 16x16x32 MFMAs; the wave
+//                  streams 32-row Q/dO tiles of every query head of the group
+//                  and accumulates dK and dV (S, dP with one key per lane;
+//                  dV^T, dK^T).  Three waves per SIMD.
 // In both kernels the bf16 probability / score-gradient registers feed the
 // next MFMA directly as its B operand (the contraction order is free), and
 // the transposed A operands (K^T, dO^T, Q^T) come from gfx950's transposing
