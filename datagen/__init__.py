@@ -37,6 +37,10 @@ __all__ = [
     "make_decode_inputs",
     "make_bwd_inputs",
     "make_serve_inputs",
+    "fp8_e4m3_bits",
+    "f64_from_fp8_e4m3_bits",
+    "quantize_fp8_e4m3",
+    "make_fp8_fwd_inputs",
     "serve_config",
     "row_subset",
 ]
@@ -177,6 +181,60 @@ def make_serve_inputs(cfg: AttnConfig):
         cfg.input_scale)
     lens = np.random.default_rng(cfg.seed + 1).integers(cfg.min_len, cfg.Nk + 1, size=cfg.B)
     return q, k, v, lens.astype(np.int32)
+
+
+# OCP fp8 e4m3 ("e4m3fn"): 1 sign bit, 4 exponent bits (bias 7), 3 mantissa
+# bits; codes 0x7F and 0xFF are NaN, there is no infinity, 448 is the largest
+# finite value.  Input preparation only: the encoder rounds to nearest, ties
+# to the even code, and saturates at +-448.
+def _e4m3_positive_values():
+    codes = np.arange(0x7F, dtype=np.int64)          # 0x00 .. 0x7E
+    e = codes >> 3
+    m = codes & 7
+    return np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+
+
+_E4M3_POS = _e4m3_positive_values()
+
+
+def fp8_e4m3_bits(x) -> np.ndarray:
+    """float array -> uint8 e4m3 codes (round to nearest even, saturate)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), _E4M3_POS[-1])
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, len(_E4M3_POS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0) & (hi != lo))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(x) & (code != 0), code | 0x80, code).astype(np.uint8)
+
+
+def f64_from_fp8_e4m3_bits(bits) -> np.ndarray:
+    """uint8 e4m3 codes (no NaN codes) -> float64 (exact)."""
+    bits = np.asarray(bits, dtype=np.uint8)
+    v = _E4M3_POS[(bits & 0x7F).astype(np.int64)]
+    return np.where(bits & 0x80, -v, v)
+
+
+def quantize_fp8_e4m3(x):
+    """Per-tensor quantisation: descale = max|x| / 448, bytes = e4m3(x / descale).
+    Returns (uint8 codes, descale as a Python float)."""
+    x = np.asarray(x, dtype=np.float64)
+    amax = float(np.abs(x).max()) if x.size else 0.0
+    descale = amax / 448.0 if amax > 0 else 1.0
+    return fp8_e4m3_bits(x / descale), descale
+
+
+def make_fp8_fwd_inputs(cfg: AttnConfig):
+    """The forward inputs of a workload (the same bf16 draws) quantised per
+    tensor to fp8 e4m3: ((q8, k8, v8), (q_descale, k_descale, v_descale))."""
+    out, scales = [], []
+    for bits in make_fwd_inputs(cfg):
+        codes, ds = quantize_fp8_e4m3(f64_from_bf16_bits(bits))
+        out.append(codes)
+        scales.append(ds)
+    return tuple(out), tuple(scales)
 
 
 def make_decode_inputs(cfg: AttnConfig):

@@ -20,8 +20,8 @@ __all__ = [
     "fa_last_hip_error", "fa_fwd_kernel_name", "fa_decode_kernel_name",
     "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_kernel_name",
     "fa_decode_serve", "fa_decode_serve_workspace_size", "fa_decode_serve_num_splits",
-    "fa_decode_serve_kernel_name",
-    "fwd", "decode", "decode_serve", "bwd", "EXPORTED_SYMBOLS", "LIB_PATH",
+    "fa_decode_serve_kernel_name", "fa_fwd_fp8", "fa_fwd_fp8_kernel_name",
+    "fwd", "fwd_fp8", "decode", "decode_serve", "bwd", "EXPORTED_SYMBOLS", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -55,6 +55,9 @@ _SIGNATURES = {
     "fa_decode_serve_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "fa_decode_serve_num_splits": (_i, [_i, _i, _i, _i, _i, _i]),
     "fa_decode_serve_kernel_name": (_cs, [_i, _i, _i, _i]),
+    "fa_fwd_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _f, _f, _f, _i,
+                        _vp]),
+    "fa_fwd_fp8_kernel_name": (_cs, [_i, _i]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -114,6 +117,17 @@ def fa_decode_serve(q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d,
     return lib().fa_decode_serve(q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Nq, Nk, d,
                                  scale, int(causal), num_splits, workspace, workspace_bytes,
                                  stream)
+
+
+def fa_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, q_descale, k_descale, v_descale,
+               causal, stream=None):
+    return lib().fa_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, q_descale, k_descale,
+                            v_descale, int(causal), stream)
+
+
+def fa_fwd_fp8_kernel_name(d, causal):
+    r = lib().fa_fwd_fp8_kernel_name(d, int(causal))
+    return r.decode() if r else None
 
 
 def fa_decode_serve_workspace_size(B, Hq, Nq, d, num_splits):
@@ -313,4 +327,31 @@ def decode_serve(q, k_cache, v_cache, seqlens=None, causal=False, scale=None, nu
                          _stream_ptr())
     if rc != FA_OK:
         raise FAError(rc, "fa_decode_serve")
+    return out, lse
+
+
+def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal=False, scale=None, out=None,
+            lse=None):
+    """O, LSE of attention on fp8 e4m3 inputs (uint8 tensors [B][H][N][d],
+    real value = byte value * descale) -> O bf16, LSE fp32."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.uint8 or t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous uint8 (fp8 e4m3 bytes) device tensor "
+                             "[B][H][N][d]")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B][Hkv][Nk][d] with q's B and d")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    rc = fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B,
+                    Hq, Hkv, Nq, Nk, d, float(scale), float(q_descale), float(k_descale),
+                    float(v_descale), int(bool(causal)), _stream_ptr())
+    if rc != FA_OK:
+        raise FAError(rc, "fa_fwd_fp8")
     return out, lse

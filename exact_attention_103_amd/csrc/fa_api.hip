@@ -104,6 +104,58 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return e == hipSuccess ? FA_OK : hip_fail(e);
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+               int Hq, int Hkv, int Nq, int Nk, int d, float scale, float q_descale,
+               float k_descale, float v_descale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (causal && Nq > Nk) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (!scale_ok(scale) || !scale_ok(q_descale) || !scale_ok(k_descale) || !scale_ok(v_descale))
+    return FA_ERR_SCALE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  const int64_t q_bytes = checked_product({B, Hq, Nq, d});
+  const int64_t kv_bytes = checked_product({B, Hkv, Nk, d});
+  const int64_t o_bytes = checked_product({B, Hq, Nq, d, 2});
+  const int64_t lse_bytes = checked_product({B, Hq, Nq, 4});
+  const int bm = fa::fwd_fp8_rows_per_block();
+  const int64_t grid = checked_product({(Nq + bm - 1) / bm, B, Hq});
+  if (q_bytes < 0 || kv_bytes < 0 || o_bytes < 0 || lse_bytes < 0 || grid < 0 ||
+      grid > INT32_MAX)
+    return FA_ERR_TOO_LARGE;
+  const Span ins[3] = {span(q, q_bytes), span(k, kv_bytes), span(v, kv_bytes)};
+  const Span so = span(o, o_bytes), sl = span(lse, lse_bytes);
+  for (const Span& in : ins)
+    if (overlaps(so, in) || overlaps(sl, in)) return FA_ERR_ALIAS;
+  if (overlaps(so, sl)) return FA_ERR_ALIAS;
+
+  fa::FwdF8Params p;
+  p.q = static_cast<const uint8_t*>(q);
+  p.k = static_cast<const uint8_t*>(k);
+  p.v = static_cast<const uint8_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.group = Hq / Hkv;
+  p.c = scale * q_descale * k_descale * fa::kLog2e;
+  p.v_descale = v_descale;
+  if (!isfinite(p.c) || !(p.c > 0.f)) return FA_ERR_SCALE;
+  const hipError_t e = fa::launch_fwd_fp8(p, d, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : hip_fail(e);
+}
+
+const char* fa_fwd_fp8_kernel_name(int d, int causal) {
+  if (causal != 0 && causal != 1) return nullptr;
+  return fa::fwd_fp8_kernel_name(d, causal != 0);
+}
+
 int fa_decode_max_splits(int Nk) { return max_splits(Nk); }
 
 size_t fa_decode_workspace_size(int B, int Hq, int d, int num_splits) {

@@ -1,0 +1,327 @@
+// FP8 exact-attention forward for gfx950 (CDNA4 OCP fp8 e4m3 MFMA).
+//
+// Pages cited (short names):
+//   [Evolution]  "FlashAttention evolution" (sandeep007734.github.io,
+//                posts/flashattention-evolution)
+//   [Comparison] "FlashAttention 1-4 generation comparison"
+//                (phantomic12.github.io, inference-research)
+//
+// The same fused forward as fa_fwd.hip (tiling, online softmax, one query
+// per lane through S^T = K Q^T, deferred normalisation), with both products
+// in 8-bit floating point as FlashAttention-3 does on Hopper ([Evolution]
+// §4; [Comparison] "Notes", FA-3 entry).  Q, K and V arrive as OCP fp8
+// e4m3 values with one dequantisation factor each (real = fp8 * factor):
+//   S^T = K Q^T          v_mfma_scale_f32_32x32x64_f8f6f4 (fp8 x fp8, unit
+//                        block scales), fp32 accumulate; the three factors
+//                        and the softmax scale fold into the exponent FMA.
+//   online softmax       as in the bf16 kernel (base 2, running max and
+//                        sum in fp32, conditional rescale), so P <= 2^8.
+//   O^T += V^T P^T       P^T rounded to fp8 e4m3 in the accumulator's own
+//                        registers (4 per dword, v_cvt_pk_fp8_f32), V^T from
+//                        gfx950's 8-bit transposing LDS read.
+// The MFMA contracts lane half h, byte p of the A operand with lane half h,
+// byte p of the B operand (any consistent k assignment gives the same
+// product), so K and Q use contiguous d ranges, and V^T is read with the key
+// order that the P^T registers hold.  O = v_factor * acc / l (bf16), LSE in
+// natural log of the scaled scores.
+
+#include "fa_internal.h"
+
+#include <math.h>
+
+namespace fa {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr float kF8RescaleThreshold = 8.0f;   // P stays <= 2^8 < 448 (e4m3 maximum)
+
+template <int D, int NW>
+struct F8Shape {
+  static constexpr int BN = 64;            // keys per tile (one PV k-step)
+  static constexpr int BM = 32 * NW;       // query rows per workgroup
+  static constexpr int RB = D;             // bytes per K or V row
+  static constexpr int CPR = D / 16;       // 16-byte chunks per row
+  static constexpr int KSTEPS = D / 64;    // 32x32x64 k-steps over d
+  static constexpr int KB = BN / 32;       // 32-key blocks per tile
+  static constexpr int DB = D / 32;        // 32-row d blocks of O^T
+  static constexpr int TILE = BN * RB;
+  static constexpr int BLKS = TILE / 1024;
+  static constexpr int LOADS = (BLKS + NW - 1) / NW;
+  static_assert(D % 64 == 0, "fp8 head dim");
+};
+
+// LDS tiles: 16-byte chunk c of row r at c ^ ((r / 2) mod CPR).
+template <int RB>
+__device__ __forceinline__ int f8_xor(int r) { return (r >> 1) & (RB / 16 - 1); }
+
+__device__ __forceinline__ float f8_half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float f8_half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void f8_load_tile(const uint8_t* base, int j0, int Nk, lds_char* tile,
+                                             int wave, int lane) {
+  using S = F8Shape<D, NW>;
+#pragma unroll
+  for (int i = 0; i < S::LOADS; ++i) {
+    const int blk = i * NW + wave;
+    if (S::BLKS % NW != 0 && blk >= S::BLKS) break;
+    const int P = blk * 64 + lane;
+    const int row = P / S::CPR;
+    const int c = (P % S::CPR) ^ f8_xor<S::RB>(row);
+    const int key = min(j0 + row, Nk - 1);
+    __builtin_amdgcn_global_load_lds(base + (size_t)key * D + c * 16, tile + blk * 1024, 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ v8i f8_mfma_operand(v4i lo, v4i hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int D, int NW, bool CAUSAL>
+__device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0, lds_char* kb1,
+                                             lds_char* vb0, lds_char* vb1) {
+  using S = F8Shape<D, NW>;
+  constexpr int BN = S::BN;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int hl = lane >> 5;
+  const int n = lane & 31;
+
+  const int BH = p.B * p.Hq;
+  const int nqb = (p.Nq + S::BM - 1) / S::BM;
+  const int bh = blockIdx.x % BH;
+  const int qi = blockIdx.x / BH;
+  const int qblk = CAUSAL ? (nqb - 1 - qi) : qi;
+  const int b = bh / p.Hq;
+  const int h = bh - b * p.Hq;
+  const int g = h / p.group;
+  const int q0 = qblk * S::BM;
+  const int qw = q0 + 32 * wave;
+  const int row = qw + n;
+  const int off = p.Nk - p.Nq;
+
+  const uint8_t* kbase = p.k + (size_t)(b * p.Hkv + g) * p.Nk * D;
+  const uint8_t* vbase = p.v + (size_t)(b * p.Hkv + g) * p.Nk * D;
+
+  int nkt = (p.Nk + BN - 1) / BN;
+  if (CAUSAL) nkt = min(nkt, (min(q0 + S::BM, p.Nq) - 1 + off) / BN + 1);
+
+  // Q^T B operand: lane (hl, n) holds Q[row][64t + 32hl .. +31].  Rows past
+  // Nq are zero.
+  v8i qf[S::KSTEPS];
+#pragma unroll
+  for (int t = 0; t < S::KSTEPS; ++t) {
+    if (row < p.Nq) {
+      const uint8_t* src = p.q + ((size_t)bh * p.Nq + row) * D + 64 * t + 32 * hl;
+      qf[t] = f8_mfma_operand(*reinterpret_cast<const v4i*>(src),
+                              *reinterpret_cast<const v4i*>(src + 16));
+    } else {
+      qf[t] = v8i{};
+    }
+  }
+
+  // K A-operand reads: row 32kb + n, chunks 4t + 2hl and +1.
+  const int kx = f8_xor<S::RB>(n);
+  // V^T A-operand reads (8-bit transposing loads): source lane s of a
+  // 16-lane group (hl, g1) addresses key row vrow + 16u and 8 bytes at
+  // column 32db + 16g1 + 8(s&1); lane i of the group then receives column
+  // 32db + 16g1 + i of the 8 rows its group's sources address, in source
+  // order, which is the key order of the P^T registers 8u .. 8u+7.
+  const int s16 = lane & 15;
+  const int g1 = (lane >> 4) & 1;
+  const int qsel = ((s16 & 7) >> 1) + 4 * (s16 >> 3);
+  const int vrow = 8 * (qsel >> 2) + 4 * hl + (qsel & 3);
+  const int vx = f8_xor<S::RB>(vrow);
+  int voff[S::DB];
+#pragma unroll
+  for (int db = 0; db < S::DB; ++db)
+    voff[db] = vrow * S::RB + (((2 * db + g1) ^ vx) << 4) + 8 * (s16 & 1);
+
+  f32x16 oacc[S::DB];
+#pragma unroll
+  for (int db = 0; db < S::DB; ++db) oacc[db] = f32x16{};
+  float m_run = -1e30f;
+  float l_run[2] = {0.f, 0.f};
+
+  auto s_tile = [&](const lds_char* kt, f32x16 (&sacc)[S::KB]) {
+#pragma unroll
+    for (int kb = 0; kb < S::KB; ++kb) {
+      sacc[kb] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < S::KSTEPS; ++t) {
+        const lds_char* rp = kt + (kb * 32 + n) * S::RB;
+        const v4i lo = *(const __attribute__((address_space(3))) v4i*)(rp + (((4 * t + 2 * hl) ^ kx) << 4));
+        const v4i hi = *(const __attribute__((address_space(3))) v4i*)(rp + (((4 * t + 2 * hl + 1) ^ kx) << 4));
+        sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f8_mfma_operand(lo, hi), qf[t],
+                                                                  sacc[kb], 0, 0, 0, 127, 0, 127);
+      }
+    }
+  };
+  auto needs_mask = [&](int t) {
+    const int t0 = t * BN;
+    return (t0 + BN > p.Nk) || (CAUSAL && t0 + BN - 1 > qw + off);
+  };
+  auto mask_tile = [&](f32x16 (&sacc)[S::KB], int t) {
+    const int lim = (CAUSAL ? min(p.Nk - 1, row + off) : p.Nk - 1) - t * BN - 4 * hl;
+#pragma unroll
+    for (int kb = 0; kb < S::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
+  };
+  auto tile_max = [&](const f32x16 (&sacc)[S::KB]) {
+    float x = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < S::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) x = fmaxf(fmaxf(x, sacc[kb][r]), sacc[kb][r + 1]);
+    return f8_half_max(x) * p.c;
+  };
+
+  float mnext;
+  auto step = [&](const lds_char* kr, const lds_char* vr, lds_char* kw, lds_char* vw,
+                  f32x16 (&sc)[S::KB], f32x16 (&sn)[S::KB], int j) {
+    const int j0 = j * BN;
+    if (needs_mask(j)) {
+      mask_tile(sc, j);
+      mnext = tile_max(sc);
+    }
+    const float m_new = fmaxf(m_run, mnext);
+    if (__any(m_new > m_run + kF8RescaleThreshold)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run[0] *= alpha;
+      l_run[1] *= alpha;
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m_run = m_new;
+    }
+    if (j + 2 < nkt) f8_load_tile<D, NW>(kbase, j0 + 2 * BN, p.Nk, kw, wave, lane);
+    if (j + 1 < nkt) f8_load_tile<D, NW>(vbase, j0 + BN, p.Nk, vw, wave, lane);
+
+    // S^T of tile j+1 on the MFMA pipe next to tile j's softmax.
+    s_tile(kr, sn);
+
+    // P^T = 2^(S*c - m) rounded to fp8: dword w holds keys of block w/4,
+    // registers 4(w%4) .. +3, which the V^T reads below follow.
+    const float nm = -m_run;
+    v8i pf;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int kb = w >> 2, r0 = 4 * (w & 3);
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 0], p.c, nm));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 1], p.c, nm));
+      const float e2 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 2], p.c, nm));
+      const float e3 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 3], p.c, nm));
+      l_run[0] += e0 + e2;
+      l_run[1] += e1 + e3;
+      int x = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+      x = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, x, true);
+      pf[w] = x;
+    }
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db) {
+      v8i a;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i*)(vr + voff[db] + 16 * u * S::RB));
+        a[2 * u] = t[0];
+        a[2 * u + 1] = t[1];
+      }
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf, oacc[db], 0, 0, 0, 127, 0, 127);
+    }
+    mnext = tile_max(sn);
+    __syncthreads();
+  };
+
+  f32x16 sa[S::KB], sb[S::KB];
+  f8_load_tile<D, NW>(kbase, 0, p.Nk, kb0, wave, lane);
+  f8_load_tile<D, NW>(vbase, 0, p.Nk, vb0, wave, lane);
+  if (nkt > 1) f8_load_tile<D, NW>(kbase, BN, p.Nk, kb1, wave, lane);
+  __syncthreads();
+  s_tile(kb0, sa);
+  mnext = tile_max(sa);
+  __syncthreads();
+  for (int j = 0; j < nkt; j += 2) {
+    step(kb1, vb0, kb0, vb1, sa, sb, j);
+    if (j + 1 < nkt) step(kb0, vb1, kb1, vb0, sb, sa, j + 1);
+  }
+
+  const float l_tot = f8_half_sum(l_run[0] + l_run[1]);
+  if (row < p.Nq) {
+    const float inv = p.v_descale / l_tot;
+    uint16_t* orow = p.o + ((size_t)bh * p.Nq + row) * D;
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x2 lo = {(__bf16)(oacc[db][4 * r4 + 0] * inv), (__bf16)(oacc[db][4 * r4 + 1] * inv)};
+        bf16x2 hi = {(__bf16)(oacc[db][4 * r4 + 2] * inv), (__bf16)(oacc[db][4 * r4 + 3] * inv)};
+        uint2 w;
+        w.x = __builtin_bit_cast(unsigned, lo);
+        w.y = __builtin_bit_cast(unsigned, hi);
+        *reinterpret_cast<uint2*>(orow + 32 * db + 8 * r4 + 4 * hl) = w;
+      }
+    if (hl == 0) p.lse[(size_t)bh * p.Nq + row] = (m_run + log2f(l_tot)) * kLn2;
+  }
+}
+
+}  // namespace
+}  // namespace fa
+
+#define FA_FWD_FP8_KERNEL(NAME, D, NW, CAUSAL)                                          \
+  extern "C" __global__ void __launch_bounds__(64 * NW, 2) NAME(fa::FwdF8Params p) {   \
+    using Sh = fa::F8Shape<D, NW>;                                                     \
+    __shared__ __attribute__((aligned(1024))) char k0[Sh::TILE];                       \
+    __shared__ __attribute__((aligned(1024))) char k1[Sh::TILE];                       \
+    __shared__ __attribute__((aligned(1024))) char v0[Sh::TILE];                       \
+    __shared__ __attribute__((aligned(1024))) char v1[Sh::TILE];                       \
+    fa::fwd_fp8_body<D, NW, CAUSAL>(p, (fa::lds_char*)k0, (fa::lds_char*)k1,           \
+                                    (fa::lds_char*)v0, (fa::lds_char*)v1);             \
+  }
+
+FA_FWD_FP8_KERNEL(fa_fwd_fp8_d64_nomask, 64, 8, false)
+FA_FWD_FP8_KERNEL(fa_fwd_fp8_d64_causal, 64, 8, true)
+FA_FWD_FP8_KERNEL(fa_fwd_fp8_d128_nomask, 128, 8, false)
+FA_FWD_FP8_KERNEL(fa_fwd_fp8_d128_causal, 128, 8, true)
+
+namespace fa {
+
+int fwd_fp8_rows_per_block() { return 32 * 8; }
+
+const char* fwd_fp8_kernel_name(int d, bool causal) {
+  switch (d) {
+    case 64: return causal ? "fa_fwd_fp8_d64_causal" : "fa_fwd_fp8_d64_nomask";
+    case 128: return causal ? "fa_fwd_fp8_d128_causal" : "fa_fwd_fp8_d128_nomask";
+    default: return nullptr;
+  }
+}
+
+hipError_t launch_fwd_fp8(const FwdF8Params& p, int d, bool causal, hipStream_t s) {
+  const void* fn = nullptr;
+  switch (d) {
+    case 64: fn = causal ? (const void*)fa_fwd_fp8_d64_causal : (const void*)fa_fwd_fp8_d64_nomask; break;
+    case 128: fn = causal ? (const void*)fa_fwd_fp8_d128_causal : (const void*)fa_fwd_fp8_d128_nomask; break;
+    default: return hipErrorInvalidValue;
+  }
+  const int bm = fwd_fp8_rows_per_block();
+  const dim3 grid((unsigned)(((p.Nq + bm - 1) / bm) * p.B * p.Hq));
+  FwdF8Params arg = p;
+  void* args[] = {&arg};
+  return hipLaunchKernel(fn, grid, dim3(64 * 8), args, 0, s);
+}
+
+}  // namespace fa

@@ -29,6 +29,21 @@ struct FwdParams {
   float c;       // scale * log2(e)
 };
 
+// Arguments of one fp8 forward launch: q, k, v are OCP fp8 e4m3 bytes
+// [B][H][N][d] (real value = byte value * its descale factor); o bf16, lse
+// fp32.  c = scale * q_descale * k_descale * log2(e).
+struct FwdF8Params {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  uint16_t* o;
+  float* lse;
+  int B, Hq, Hkv, Nq, Nk;
+  int group;
+  float c;
+  float v_descale;
+};
+
 // Arguments of one split-KV decode (split kernel + merge kernel).
 struct DecodeParams {
   const uint16_t* q;      // [B][Hq][d]
@@ -81,6 +96,9 @@ int decode_serve_group_tile(int group, int nq);
 const char* fwd_kernel_name(int d, bool causal, int Nq, int Nk);
 const char* decode_kernel_name(int d, int group, int stage);
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s);
+hipError_t launch_fwd_fp8(const FwdF8Params& p, int d, bool causal, hipStream_t s);
+const char* fwd_fp8_kernel_name(int d, bool causal);
+int fwd_fp8_rows_per_block();
 const char* bwd_kernel_name(int d, bool causal, int stage);
 bool bwd_supported_d(int d);
 int bwd_dq_grid_blocks(int B, int Hq, int Nq);

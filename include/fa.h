@@ -40,7 +40,8 @@ enum fa_status {
   FA_ERR_NULL = -1,       /* a required pointer is NULL                      */
   FA_ERR_SHAPE = -2,      /* B, H or N <= 0, Hq % Hkv != 0, causal && Nq > Nk,
                              serving decode Nq outside 1..16                 */
-  FA_ERR_HEAD_DIM = -3,   /* d not in {32, 64, 128, 256} ({32, 64, 128} bwd) */
+  FA_ERR_HEAD_DIM = -3,   /* d not in {32, 64, 128, 256} ({32, 64, 128} bwd,
+                             {64, 128} fp8 forward)                           */
   FA_ERR_ALIGN = -4,      /* a tensor pointer is not 16-byte aligned         */
   FA_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required         */
   FA_ERR_SPLITS = -6,     /* num_splits outside 0 .. fa_decode_max_splits()  */
@@ -79,6 +80,33 @@ enum fa_status {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
            int causal, void* stream);
+
+/*
+ * fa_fwd_fp8 -- the forward of fa_fwd with fp8 inputs and fp8 products.
+ *
+ * FlashAttention-3 runs both products in 8-bit floating point ([Evolution]
+ * §4; [Comparison] "Notes", FA-3 entry).  Here q, k, v are OCP fp8 e4m3
+ * bytes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, largest
+ * value 448) with one dequantisation factor per tensor: the real inputs are
+ * byte value * q_descale (k_descale, v_descale).  The function computed is
+ * fa_fwd's on those real values; inside, S = Q K^T is exact up to fp32
+ * accumulation and P is rounded to e4m3 before P V, which bounds the error
+ * of each output element by about 2^-4 * max|v| (plus bf16 rounding of O).
+ * Incoherent processing (a random Hadamard rotation of Q and K before
+ * quantisation) is the caller's preprocessing and is not applied here.
+ *
+ *   q         fp8 e4m3 [B][Hq][Nq][d]
+ *   k, v      fp8 e4m3 [B][Hkv][Nk][d]
+ *   o         bf16 [B][Hq][Nq][d]     output
+ *   lse       fp32 [B][Hq][Nq]        output, natural log of the scaled scores
+ *   d         64 or 128
+ *   scale, q_descale, k_descale, v_descale  finite, > 0
+ * Errors as fa_fwd (FA_ERR_HEAD_DIM for d other than 64, 128).
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+               float q_descale, float k_descale, float v_descale, int causal,
+               void* stream);
 
 /*
  * Split-KV decode ([Evolution] §6, Flash-Decoding): one query row per
@@ -221,6 +249,8 @@ const char* fa_bwd_kernel_name(int d, int causal, int stage);
 /* fa_decode_serve_kernel_name: stage 0 = split kernel (depends on the query
  * heads per KV head and on Nq), stage 1 = merge kernel. */
 const char* fa_decode_serve_kernel_name(int d, int hq_per_kv, int Nq, int stage);
+/* fa_fwd_fp8_kernel_name: the fp8 forward kernel for d and causal. */
+const char* fa_fwd_fp8_kernel_name(int d, int causal);
 
 #ifdef __cplusplus
 }

@@ -113,6 +113,32 @@ def test_serve_helpers():
     assert fa.fa_decode_serve_num_splits(8, 32, 8, 17, 32768, 128) == -2
 
 
+def test_fp8_names_and_quantiser():
+    assert fa.fa_fwd_fp8_kernel_name(128, 1) == "fa_fwd_fp8_d128_causal"
+    assert fa.fa_fwd_fp8_kernel_name(64, 0) == "fa_fwd_fp8_d64_nomask"
+    assert fa.fa_fwd_fp8_kernel_name(32, 0) is None
+    assert fa.fa_fwd_fp8_kernel_name(128, 2) is None
+
+
+def test_fp8_encoder_matches_torch():
+    """The input quantiser's e4m3 codes equal torch's float8_e4m3fn cast (round
+    to nearest even) on in-range values, including ties and subnormals."""
+    import numpy as np
+    import torch
+    import datagen
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(20000) * 50, rng.standard_normal(2000) * 0.01,
+                        np.arange(-448, 449, 0.0625), (np.arange(1, 64) + 0.5) * 2.0 ** -9])
+    x = np.clip(x, -448, 448)
+    ours = datagen.fp8_e4m3_bits(x)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    # torch keeps -0 as 0x80; the encoder maps every zero to 0x00
+    ref = np.where(ref == 0x80, 0, ref)
+    assert np.array_equal(ours, ref)
+    assert np.array_equal(datagen.f64_from_fp8_e4m3_bits(ours),
+                          torch.from_numpy(ours).view(torch.float8_e4m3fn).to(torch.float64).numpy())
+
+
 def test_workspace_and_splits():
     assert fa.fa_decode_workspace_size(8, 32, 128, 32) == 4 * 8 * 32 * 32 * 129
     assert fa.fa_decode_workspace_size(8, 32, 100, 32) == 0
@@ -258,3 +284,20 @@ def _serve(**kw):
 ])
 def test_serve_rejects(kw, code):
     assert _serve(**kw) == code
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), -1), (dict(o=0), -1), (dict(B=0), -2), (dict(Hq=3), -2), (dict(causal=2), -2),
+    (dict(Nq=65, Nk=64), -2), (dict(d=32), -3), (dict(d=256), -3),
+    (dict(scale=0.0), -8), (dict(qd=0.0), -8), (dict(kd=math.inf), -8), (dict(vd=-1.0), -8),
+    (dict(q=Q + 8), -4), (dict(o=O + 4), -4),
+    (dict(o=Q), -9), (dict(lse=K + 16), -9),
+])
+def test_fp8_rejects(kw, code):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, Hq=4, Hkv=2, Nq=64, Nk=64, d=128, scale=0.125,
+             qd=0.01, kd=0.01, vd=0.01, causal=1)
+    a.update(kw)
+    assert fa.fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                         a["Nq"], a["Nk"], a["d"], a["scale"], a["qd"], a["kd"], a["vd"],
+                         a["causal"], None) == code
