@@ -12,6 +12,9 @@ same stream, inputs already resident in HBM.  Prints one JSON line:
             decode carries its own roofline against 8 TB/s HBM
   cpu_baseline  the float64 oracle on a bounded sample of the same workload,
             timed on the host cores (rank 0, one GPU)
+  fp8       after the timed steps: fa_fwd_fp8 on the same prefill quantised
+            per tensor to fp8 e4m3, timed per call; its own roofline against
+            the 5 PFLOP/s dense fp8 MFMA peak
   bwd       after the timed steps: the backward pass (fa_bwd) of the same
             prefill, fed the last step's O and LSE and a seeded dO, timed
             over its own launches; TFLOP/s counts the algorithmic 5 products
@@ -19,6 +22,7 @@ same stream, inputs already resident in HBM.  Prints one JSON line:
             recomputation performs
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bwd]
+                      [--no-fp8]
 """
 
 from __future__ import annotations
@@ -39,6 +43,7 @@ import datagen  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 METRIC = "fused attn fwd TFLOP/s (% bf16 MFMA peak); split-KV decode HBM GB/s"
 
 
@@ -128,6 +133,45 @@ def _blas_threads():
     return os.cpu_count()
 
 
+def fp8_leg(fa, cfg, stream, steps, warmup=20):
+    """fa_fwd_fp8 on the prefill quantised per tensor to fp8 e4m3 (the same
+    draws as the bf16 leg), timed per call with HIP events."""
+    import torch
+    (q8, k8, v8), sc = datagen.make_fp8_fwd_inputs(cfg)
+    dq, dk, dv = (torch.from_numpy(np.ascontiguousarray(x)).to("cuda:0") for x in (q8, k8, v8))
+    o8 = torch.empty((cfg.B, cfg.Hq, cfg.Nq, cfg.d), dtype=torch.bfloat16, device="cuda")
+    l8 = torch.empty((cfg.B, cfg.Hq, cfg.Nq), dtype=torch.float32, device="cuda")
+    sp = stream.cuda_stream
+
+    def call():
+        rc = fa.fa_fwd_fp8(dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), o8.data_ptr(), l8.data_ptr(),
+                           cfg.B, cfg.Hq, cfg.Hkv, cfg.Nq, cfg.Nk, cfg.d, cfg.scale, sc[0], sc[1],
+                           sc[2], int(cfg.causal), sp)
+        if rc:
+            raise fa.FAError(rc, "fa_fwd_fp8")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in evs:
+        e[0].record(stream)
+        call()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[1]) for e in evs]
+    f_ms = float(np.mean(ms))
+    tf = cfg.flops() / (f_ms * 1e-3) / 1e12
+    srcs = ["exact_attention_103_amd/csrc/fa_fwd_fp8.hip", "exact_attention_103_amd/csrc/fa_internal.h"]
+    kname = fa.fa_fwd_fp8_kernel_name(cfg.d, int(cfg.causal))
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(f_ms, 4),
+            "ms_min": round(min(ms), 4), "dtype": "fp8 e4m3 (per-tensor scales), fp32 accumulate",
+            "kernel": kname,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                         "traffic": _traffic(kname, srcs)}}
+
+
 def bwd_leg(fa, cfg, q, k, v, o, lse, stream, steps, warmup=10):
     """Backward of the prefill: fa_bwd fed the forward's O and LSE and a
     seeded dO, timed per call with HIP events on the launch stream."""
@@ -188,6 +232,7 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="decode splits (0 = heuristic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 forward leg")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="instead of the benchmark, run three plain device-to-device "
                          "copies of BYTES bytes (reference dispatches for HBM counters)")
@@ -313,6 +358,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not args.no_fp8:
+        out["fp8"] = fp8_leg(fa, fcfg, stream, args.steps)
     if not args.no_bwd:
         out["bwd"] = bwd_leg(fa, fcfg, q, k, v, o, lse, stream, args.steps)
     if not args.no_cpu_baseline:

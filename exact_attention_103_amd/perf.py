@@ -78,6 +78,23 @@ def main():
                           "tflops": round(flop / ms / 1e9, 1),
                           "pct_of_2500": round(100 * flop / ms / 1e9 / 2500, 1)}), flush=True)
         del q, k, v, o, lse
+    for name, B, H, N, d, causal, sc in FWD:
+        if d not in (64, 128):
+            continue
+        # fp8 forward on random e4m3 codes of magnitude <= 2 (speed only).
+        q8 = torch.randint(0, 0x41, (B, H, N, d), dtype=torch.uint8, device="cuda")
+        k8 = torch.randint(0, 0x41, (B, H, N, d), dtype=torch.uint8, device="cuda")
+        v8 = torch.randint(0, 0x41, (B, H, N, d), dtype=torch.uint8, device="cuda")
+        o = torch.empty(B, H, N, d, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(B, H, N, device="cuda", dtype=torch.float32)
+        ms = _time(lambda: fa.fwd_fp8(q8, k8, v8, 1.0, 1.0, 1.0, causal=causal, out=o, lse=lse),
+                   args.iters, args.warmup)
+        flop = 4.0 * B * H * N * N * d / (2 if causal else 1)
+        print(json.dumps({"workload": name + "_fp8", "B": B, "H": H, "N": N, "d": d,
+                          "causal": causal, "kernel": fa.fa_fwd_fp8_kernel_name(d, int(causal)),
+                          "ms": round(ms, 4), "tflops": round(flop / ms / 1e9, 1),
+                          "pct_of_5000": round(100 * flop / ms / 1e9 / 5000, 1)}), flush=True)
+        del q8, k8, v8, o, lse
     for B, Hq, Hkv, Nk, d, S in DECODE:
         q = torch.randn(B, Hq, d, device="cuda").to(torch.bfloat16)
         kc = torch.randn(B, Hkv, Nk, d, device="cuda").to(torch.bfloat16)
