@@ -237,6 +237,21 @@ def make_fp8_fwd_inputs(cfg: AttnConfig):
     return tuple(out), tuple(scales)
 
 
+def drifting_bf16(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int, slope: float,
+                  noise: float = 0.1):
+    """Inputs whose scores drift along the key axis: q = 0.5 + noise*z and
+    k_j = slope*j/(0.5*sqrt(d)*log2 e) + noise*z per element, v ~ N(0,1), all
+    rounded to bf16.  With the softmax scale 1/sqrt(d) the score of key j in
+    base-2 units is then about slope*j (negative slope: falling scores), so a
+    row's largest score keeps moving as its keys are scanned."""
+    rng = np.random.default_rng(seed)
+    q = 0.5 + noise * rng.standard_normal((B, Hq, N, d))
+    t = slope * np.arange(N) / (0.5 * np.sqrt(d) * np.log2(np.e))
+    k = t[None, None, :, None] + noise * rng.standard_normal((B, Hkv, N, d))
+    v = rng.standard_normal((B, Hkv, N, d))
+    return [bf16_bits_from_f32(x.astype(np.float32)) for x in (q, k, v)]
+
+
 def make_decode_inputs(cfg: AttnConfig):
     """bf16 bits for q [B][Hq][d], k_cache and v_cache [B][Hkv][Nk][d]."""
     return gaussian_bf16(

@@ -14,8 +14,10 @@
 //   S^T = K Q^T          v_mfma_scale_f32_32x32x64_f8f6f4 (fp8 x fp8, unit
 //                        block scales), fp32 accumulate; the three factors
 //                        and the softmax scale fold into the exponent FMA.
-//   online softmax       as in the bf16 kernel (base 2, running max and
-//                        sum in fp32, conditional rescale), so P <= 2^8.
+//   online softmax       base 2, running reference maximum and sum in
+//                        fp32, probabilities against the reference without
+//                        a per-tile row maximum: the reference only moves
+//                        when a lane's tile sum reaches 2^8 (below).
 //   O^T += V^T P^T       P^T rounded to fp8 e4m3 in the accumulator's own
 //                        registers (4 per dword, v_cvt_pk_fp8_f32), V^T from
 //                        gfx950's 8-bit transposing LDS read.
@@ -37,7 +39,15 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr float kF8RescaleThreshold = 8.0f;   // P stays <= 2^8 < 448 (e4m3 maximum)
+// A lane's 32 probabilities of a tile summing below 2^8 bounds each of them
+// below 2^8 < 448 (the e4m3 maximum).  Otherwise (the row's first tile, whose
+// reference is still -1e30 and so gives inf, or a score that rose by several
+// units) the tile's row maximum becomes the reference, the accumulator is
+// rescaled and the tile's probabilities are recomputed, now all <= 1.  Any
+// reference gives the same exact result ([Evolution] §5 and [Comparison]
+// "Workarounds": conditional rescaling); this one only bounds the range,
+// and the common path needs no row maximum at all.
+constexpr float kF8SumLimit = 256.0f;
 
 template <int D, int NW>
 struct F8Shape {
@@ -189,16 +199,46 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
     return f8_half_max(x) * p.c;
   };
 
-  float mnext;
   auto step = [&](const lds_char* kr, const lds_char* vr, lds_char* kw, lds_char* vw,
                   f32x16 (&sc)[S::KB], f32x16 (&sn)[S::KB], int j) {
     const int j0 = j * BN;
-    if (needs_mask(j)) {
-      mask_tile(sc, j);
-      mnext = tile_max(sc);
-    }
-    const float m_new = fmaxf(m_run, mnext);
-    if (__any(m_new > m_run + kF8RescaleThreshold)) {
+    if (needs_mask(j)) mask_tile(sc, j);
+    if (j + 2 < nkt) f8_load_tile<D, NW>(kbase, j0 + 2 * BN, p.Nk, kw, wave, lane);
+    if (j + 1 < nkt) f8_load_tile<D, NW>(vbase, j0 + BN, p.Nk, vw, wave, lane);
+
+    // S^T of tile j+1 on the MFMA pipe next to tile j's softmax.
+    s_tile(kr, sn);
+
+    // P^T = 2^(S*c - m) rounded to fp8: dword w holds keys of block w/4,
+    // registers 4(w%4) .. +3, which the V^T reads below follow.  The second
+    // pass runs only after the reference moved (see kF8SumLimit).
+    v8i pf;
+    float t0, t1;
+    for (int pass = 0;; ++pass) {
+      const float nm = -m_run;
+      t0 = 0.f;
+      t1 = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int kb = w >> 2, r0 = 4 * (w & 3);
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 0], p.c, nm));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 1], p.c, nm));
+        const float e2 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 2], p.c, nm));
+        const float e3 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 3], p.c, nm));
+        t0 += e0 + e2;
+        t1 += e1 + e3;
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+        x = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, x, true);
+        pf[w] = x;
+      }
+      // The bit-pattern test on the next tile's scores (a NaN) is never true
+      // for finite inputs; reading them here keeps their MFMAs ahead of the
+      // branch, next to this tile's exponentials.
+      bool bad = !(t0 + t1 < kF8SumLimit);
+#pragma unroll
+      for (int kb = 0; kb < S::KB; ++kb) bad = bad || __builtin_bit_cast(int, sn[kb][15]) == -1;
+      if (__builtin_expect(!__any(bad) || pass > 0, 1)) break;
+      const float m_new = fmaxf(m_run, tile_max(sc));
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run[0] *= alpha;
       l_run[1] *= alpha;
@@ -208,29 +248,8 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       m_run = m_new;
     }
-    if (j + 2 < nkt) f8_load_tile<D, NW>(kbase, j0 + 2 * BN, p.Nk, kw, wave, lane);
-    if (j + 1 < nkt) f8_load_tile<D, NW>(vbase, j0 + BN, p.Nk, vw, wave, lane);
-
-    // S^T of tile j+1 on the MFMA pipe next to tile j's softmax.
-    s_tile(kr, sn);
-
-    // P^T = 2^(S*c - m) rounded to fp8: dword w holds keys of block w/4,
-    // registers 4(w%4) .. +3, which the V^T reads below follow.
-    const float nm = -m_run;
-    v8i pf;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const int kb = w >> 2, r0 = 4 * (w & 3);
-      const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 0], p.c, nm));
-      const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 1], p.c, nm));
-      const float e2 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 2], p.c, nm));
-      const float e3 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 3], p.c, nm));
-      l_run[0] += e0 + e2;
-      l_run[1] += e1 + e3;
-      int x = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
-      x = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, x, true);
-      pf[w] = x;
-    }
+    l_run[0] += t0;
+    l_run[1] += t1;
 #pragma unroll
     for (int db = 0; db < S::DB; ++db) {
       v8i a;
@@ -243,7 +262,6 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
       }
       oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf, oacc[db], 0, 0, 0, 127, 0, 127);
     }
-    mnext = tile_max(sn);
     __syncthreads();
   };
 
@@ -253,7 +271,6 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
   if (nkt > 1) f8_load_tile<D, NW>(kbase, BN, p.Nk, kb1, wave, lane);
   __syncthreads();
   s_tile(kb0, sa);
-  mnext = tile_max(sa);
   __syncthreads();
   for (int j = 0; j < nkt; j += 2) {
     step(kb1, vb0, kb0, vb1, sa, sb, j);

@@ -111,6 +111,26 @@ def test_fp8_train_sampled():
     _workload("train_c", [(3, 5)], 256)
 
 
+@pytest.mark.parametrize("slope", [0.2, 1.0, -1.0])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_drifting_scores(slope, d):
+    """Rising scores exceed the reference maximum by far more than 2^8 in
+    tile after tile, so the tile's probabilities are redone against a new
+    reference in the middle of rows; falling scores never move it."""
+    B, H, N = 1, 2, 300
+    bits = datagen.drifting_bf16(60 + d, B, H, H, N, d, slope)
+    quant = [datagen.quantize_fp8_e4m3(datagen.f64_from_bf16_bits(x)) for x in bits]
+    q8, k8, v8 = (c for c, _ in quant)
+    sc = tuple(s for _, s in quant)
+    qd, kd, vd = (datagen.f64_from_fp8_e4m3_bits(c) * s for c, s in zip((q8, k8, v8), sc))
+    for causal in (False, True):
+        tag = f"fp8 drift slope={slope} d={d} causal={causal}"
+        announce(tag)
+        o, lse = _run(q8, k8, v8, sc, 1 / np.sqrt(d), causal)
+        o_ref, lse_ref = oracle.attention_ref(qd, kd, vd, 1 / np.sqrt(d), causal)
+        _check(tag, o, lse, o_ref, lse_ref, np.abs(vd).max())
+
+
 def test_fp8_deterministic():
     import torch
     announce("fp8 determinism")

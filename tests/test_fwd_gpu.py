@@ -188,6 +188,23 @@ def test_fwd_large_logits_stay_finite():
         assert_parity(f"large logits causal={causal}", o, lse, o_ref, lse_ref)
 
 
+@pytest.mark.parametrize("slope", [0.2, 1.0, -1.0])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_drifting_scores(slope, d):
+    """Scores rising by 0.2 or 1 (base 2) per key move each row's maximum by
+    13..64 per 64-key tile, so the accumulator is rescaled in the middle of
+    rows, tile after tile; falling scores leave the first tile's maximum in
+    place and push later probabilities to underflow."""
+    B, H, N = 1, 2, 300
+    qb, kb, vb = datagen.drifting_bf16(40 + d, B, H, H, N, d, slope)
+    for causal in (False, True):
+        tag = f"drift slope={slope} d={d} causal={causal}"
+        announce(tag)
+        o, lse = _run(qb, kb, vb, causal, 1 / math.sqrt(d))
+        o_ref, lse_ref = oracle.attention_ref(*_f64(qb, kb, vb), 1 / math.sqrt(d), causal)
+        assert_parity(tag, o, lse, o_ref, lse_ref)
+
+
 def test_fwd_repeat_runs_are_bit_identical():
     announce("fwd determinism")
     import torch
