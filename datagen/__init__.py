@@ -252,6 +252,24 @@ def drifting_bf16(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int, slope: f
     return [bf16_bits_from_f32(x.astype(np.float32)) for x in (q, k, v)]
 
 
+def random_signs(seed: int, d: int) -> np.ndarray:
+    """The random ±1 signs of the incoherent-processing rotation, int8 [d]
+    (drawn here and passed to both sides as an input)."""
+    rng = np.random.default_rng(seed)
+    return np.where(rng.random(d) < 0.5, -1, 1).astype(np.int8)
+
+
+def outlier_bf16(seed: int, shape, channels=(3, 77), gain: float = 20.0):
+    """N(0,1) bf16 bits with a few head-dim channels scaled by `gain`: the
+    outlier pattern that incoherent processing is meant for."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(shape).astype(np.float32)
+    for c in channels:
+        if c < shape[-1]:
+            x[..., c] *= np.float32(gain)
+    return bf16_bits_from_f32(x)
+
+
 def make_decode_inputs(cfg: AttnConfig):
     """bf16 bits for q [B][Hq][d], k_cache and v_cache [B][Hkv][Nk][d]."""
     return gaussian_bf16(
