@@ -21,7 +21,10 @@ __all__ = [
     "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_kernel_name",
     "fa_decode_serve", "fa_decode_serve_workspace_size", "fa_decode_serve_num_splits",
     "fa_decode_serve_kernel_name", "fa_fwd_fp8", "fa_fwd_fp8_kernel_name",
-    "fwd", "fwd_fp8", "decode", "decode_serve", "bwd", "EXPORTED_SYMBOLS", "LIB_PATH",
+    "fa_fwd_fp8_devscale", "fa_fp8_quantize", "fa_fp8_quantize_workspace_size",
+    "fa_fp8_quantize_kernel_name",
+    "fwd", "fwd_fp8", "fp8_quantize", "decode", "decode_serve", "bwd", "EXPORTED_SYMBOLS",
+    "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -58,6 +61,11 @@ _SIGNATURES = {
     "fa_fwd_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _f, _f, _f, _i,
                         _vp]),
     "fa_fwd_fp8_kernel_name": (_cs, [_i, _i]),
+    "fa_fwd_fp8_devscale": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _vp,
+                                 _vp, _i, _vp]),
+    "fa_fp8_quantize_workspace_size": (_sz, [_i, _i]),
+    "fa_fp8_quantize": (_i, [_vp, _vp, _vp, _vp, _i, _i, _vp, _sz, _vp]),
+    "fa_fp8_quantize_kernel_name": (_cs, [_i, _i]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -127,6 +135,26 @@ def fa_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, q_descale, k_desca
 
 def fa_fwd_fp8_kernel_name(d, causal):
     r = lib().fa_fwd_fp8_kernel_name(d, int(causal))
+    return r.decode() if r else None
+
+
+def fa_fwd_fp8_devscale(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, q_descale, k_descale,
+                        v_descale, causal, stream=None):
+    return lib().fa_fwd_fp8_devscale(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, q_descale,
+                                     k_descale, v_descale, int(causal), stream)
+
+
+def fa_fp8_quantize_workspace_size(rows, d):
+    return lib().fa_fp8_quantize_workspace_size(rows, d)
+
+
+def fa_fp8_quantize(x, codes, descale, signs, rows, d, workspace, workspace_bytes, stream=None):
+    return lib().fa_fp8_quantize(x, codes, descale, signs, rows, d, workspace, workspace_bytes,
+                                 stream)
+
+
+def fa_fp8_quantize_kernel_name(d, stage):
+    r = lib().fa_fp8_quantize_kernel_name(d, stage)
     return r.decode() if r else None
 
 
@@ -349,9 +377,50 @@ def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal=False, scale=None, 
         out = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    descales = (q_descale, k_descale, v_descale)
+    if all(isinstance(x, torch.Tensor) for x in descales):
+        for name, t in zip(("q_descale", "k_descale", "v_descale"), descales):
+            if t.dtype != torch.float32 or t.numel() != 1 or not t.is_cuda:
+                raise ValueError(f"{name} must be a one-element float32 device tensor")
+        rc = fa_fwd_fp8_devscale(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale),
+                                 *(t.data_ptr() for t in descales), int(bool(causal)),
+                                 _stream_ptr())
+        if rc != FA_OK:
+            raise FAError(rc, "fa_fwd_fp8_devscale")
+        return out, lse
     rc = fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B,
                     Hq, Hkv, Nq, Nk, d, float(scale), float(q_descale), float(k_descale),
                     float(v_descale), int(bool(causal)), _stream_ptr())
     if rc != FA_OK:
         raise FAError(rc, "fa_fwd_fp8")
     return out, lse
+
+
+def fp8_quantize(x, signs=None, codes=None, descale=None, workspace=None):
+    """Incoherent processing and per-tensor e4m3 quantisation of a bf16
+    device tensor [..., d] (d = 64 or 128): rotated by diag(signs) H_d /
+    sqrt(d) when `signs` (int8 device tensor [d], negative = -1) is given.
+    Returns (codes uint8 tensor of x's shape, descale float32 device tensor
+    [1]) with codes * descale approximating the rotated x."""
+    import torch
+    _check_bf16("x", x, x.dim())
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    if signs is not None and (signs.dtype != torch.int8 or tuple(signs.shape) != (d,)
+                              or not signs.is_cuda):
+        raise ValueError("signs must be an int8 device tensor of shape [d]")
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if descale is None:
+        descale = torch.empty(1, dtype=torch.float32, device=x.device)
+    need = fa_fp8_quantize_workspace_size(rows, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    rc = fa_fp8_quantize(x.data_ptr(), codes.data_ptr(), descale.data_ptr(),
+                         signs.data_ptr() if signs is not None else None, rows, d,
+                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                         _stream_ptr())
+    if rc != FA_OK:
+        raise FAError(rc, "fa_fp8_quantize")
+    return codes, descale

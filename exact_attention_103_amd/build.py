@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_decode.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_fp8_quant.hip", "fa_decode.hip", "fa_bwd.hip"]
 
 # Packed fp32 VALU forms are switched off for the device code; hipcc's host
 # pass warns that it does not know the feature, which is harmless.

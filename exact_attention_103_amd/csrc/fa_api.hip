@@ -57,6 +57,64 @@ int split_chunk(int Nk, int S) {
   return (c + fa::kDecodeChunkAlign - 1) / fa::kDecodeChunkAlign * fa::kDecodeChunkAlign;
 }
 
+// Shared by fa_fwd_fp8 (descales as values) and fa_fwd_fp8_devscale
+// (descales in device memory: qdp, kdp, vdp non-null, value factors 1).
+int fwd_fp8_common(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int Hq, int Hkv, int Nq, int Nk, int d, float scale, float q_descale,
+                   float k_descale, float v_descale, const float* qdp, const float* kdp,
+                   const float* vdp, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (causal && Nq > Nk) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (!scale_ok(scale)) return FA_ERR_SCALE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  for (const float* dp : {qdp, kdp, vdp})
+    if (dp && (reinterpret_cast<uintptr_t>(dp) & 3u) != 0) return FA_ERR_ALIGN;
+  const int64_t q_bytes = checked_product({B, Hq, Nq, d});
+  const int64_t kv_bytes = checked_product({B, Hkv, Nk, d});
+  const int64_t o_bytes = checked_product({B, Hq, Nq, d, 2});
+  const int64_t lse_bytes = checked_product({B, Hq, Nq, 4});
+  const int bm = fa::fwd_fp8_rows_per_block();
+  const int64_t grid = checked_product({(Nq + bm - 1) / bm, B, Hq});
+  if (q_bytes < 0 || kv_bytes < 0 || o_bytes < 0 || lse_bytes < 0 || grid < 0 ||
+      grid > INT32_MAX)
+    return FA_ERR_TOO_LARGE;
+  const Span ins[6] = {span(q, q_bytes), span(k, kv_bytes), span(v, kv_bytes),
+                       qdp ? span(qdp, 4) : Span{0, 0}, kdp ? span(kdp, 4) : Span{0, 0},
+                       vdp ? span(vdp, 4) : Span{0, 0}};
+  const Span so = span(o, o_bytes), sl = span(lse, lse_bytes);
+  for (const Span& in : ins)
+    if (overlaps(so, in) || overlaps(sl, in)) return FA_ERR_ALIAS;
+  if (overlaps(so, sl)) return FA_ERR_ALIAS;
+
+  fa::FwdF8Params p;
+  p.q = static_cast<const uint8_t*>(q);
+  p.k = static_cast<const uint8_t*>(k);
+  p.v = static_cast<const uint8_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.group = Hq / Hkv;
+  // Same association as the kernel's (scale * log2 e) * q_ds * k_ds, so that
+  // value and device descales give identical results.
+  p.c = scale * fa::kLog2e * q_descale * k_descale;
+  p.v_descale = v_descale;
+  p.q_ds = qdp;
+  p.k_ds = kdp;
+  p.v_ds = vdp;
+  if (!isfinite(p.c) || !(p.c > 0.f)) return FA_ERR_SCALE;
+  const hipError_t e = fa::launch_fwd_fp8(p, d, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : hip_fail(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -107,48 +165,67 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                int Hq, int Hkv, int Nq, int Nk, int d, float scale, float q_descale,
                float k_descale, float v_descale, int causal, void* stream) {
-  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
-  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
-  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
-  if (causal && Nq > Nk) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
-  if (!scale_ok(scale) || !scale_ok(q_descale) || !scale_ok(k_descale) || !scale_ok(v_descale))
+  if (!scale_ok(q_descale) || !scale_ok(k_descale) || !scale_ok(v_descale)) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     return FA_ERR_SCALE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-    return FA_ERR_ALIGN;
-  const int64_t q_bytes = checked_product({B, Hq, Nq, d});
-  const int64_t kv_bytes = checked_product({B, Hkv, Nk, d});
-  const int64_t o_bytes = checked_product({B, Hq, Nq, d, 2});
-  const int64_t lse_bytes = checked_product({B, Hq, Nq, 4});
-  const int bm = fa::fwd_fp8_rows_per_block();
-  const int64_t grid = checked_product({(Nq + bm - 1) / bm, B, Hq});
-  if (q_bytes < 0 || kv_bytes < 0 || o_bytes < 0 || lse_bytes < 0 || grid < 0 ||
-      grid > INT32_MAX)
-    return FA_ERR_TOO_LARGE;
-  const Span ins[3] = {span(q, q_bytes), span(k, kv_bytes), span(v, kv_bytes)};
-  const Span so = span(o, o_bytes), sl = span(lse, lse_bytes);
-  for (const Span& in : ins)
-    if (overlaps(so, in) || overlaps(sl, in)) return FA_ERR_ALIAS;
-  if (overlaps(so, sl)) return FA_ERR_ALIAS;
+  }
+  return fwd_fp8_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, q_descale, k_descale,
+                        v_descale, nullptr, nullptr, nullptr, causal, stream);
+}
 
-  fa::FwdF8Params p;
-  p.q = static_cast<const uint8_t*>(q);
-  p.k = static_cast<const uint8_t*>(k);
-  p.v = static_cast<const uint8_t*>(v);
-  p.o = static_cast<uint16_t*>(o);
-  p.lse = lse;
-  p.B = B;
-  p.Hq = Hq;
-  p.Hkv = Hkv;
-  p.Nq = Nq;
-  p.Nk = Nk;
-  p.group = Hq / Hkv;
-  p.c = scale * q_descale * k_descale * fa::kLog2e;
-  p.v_descale = v_descale;
-  if (!isfinite(p.c) || !(p.c > 0.f)) return FA_ERR_SCALE;
-  const hipError_t e = fa::launch_fwd_fp8(p, d, causal != 0, static_cast<hipStream_t>(stream));
+int fa_fwd_fp8_devscale(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                        const float* q_descale, const float* k_descale,
+                        const float* v_descale, int causal, void* stream) {
+  if (!q_descale || !k_descale || !v_descale) return FA_ERR_NULL;
+  return fwd_fp8_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, 1.f, 1.f, 1.f, q_descale,
+                        k_descale, v_descale, causal, stream);
+}
+
+size_t fa_fp8_quantize_workspace_size(int rows, int d) {
+  if (rows <= 0 || (d != 64 && d != 128)) return 0;
+  return 4 * (size_t)fa::quant_blocks(rows, d);
+}
+
+int fa_fp8_quantize(const void* x, void* codes, float* descale, const void* signs, int rows,
+                    int d, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !codes || !descale) return FA_ERR_NULL;
+  if (rows <= 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (!aligned16(x) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(descale) & 3u) != 0)
+    return FA_ERR_ALIGN;
+  const int64_t x_bytes = checked_product({rows, d, 2});
+  const int64_t c_bytes = checked_product({rows, d});
+  if (x_bytes < 0 || c_bytes < 0) return FA_ERR_TOO_LARGE;
+  const size_t need = fa_fp8_quantize_workspace_size(rows, d);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  const Span sx = span(x, x_bytes), sc = span(codes, c_bytes), sd = span(descale, 4);
+  const Span sw = span(workspace, static_cast<int64_t>(need));
+  const Span ss = signs ? span(signs, d) : Span{0, 0};
+  const Span outs[3] = {sc, sd, sw};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(outs[i], sx) || overlaps(outs[i], ss)) return FA_ERR_ALIAS;
+    for (int k2 = i + 1; k2 < 3; ++k2)
+      if (overlaps(outs[i], outs[k2])) return FA_ERR_ALIAS;
+  }
+
+  fa::QuantParams p;
+  p.x = static_cast<const uint16_t*>(x);
+  p.signs = static_cast<const int8_t*>(signs);
+  p.codes = static_cast<uint8_t*>(codes);
+  p.descale = descale;
+  p.partial = static_cast<float*>(workspace);
+  p.rows = rows;
+  p.nblocks = fa::quant_blocks(rows, d);
+  p.norm = signs ? sqrtf(static_cast<float>(d)) : 1.0f;
+  const hipError_t e = fa::launch_quant(p, d, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : hip_fail(e);
+}
+
+const char* fa_fp8_quantize_kernel_name(int d, int stage) {
+  if (stage != 0 && stage != 1) return nullptr;
+  return fa::quant_kernel_name(d, stage);
 }
 
 const char* fa_fwd_fp8_kernel_name(int d, int causal) {

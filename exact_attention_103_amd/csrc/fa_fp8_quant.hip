@@ -1,0 +1,206 @@
+// FP8 input step for gfx950: incoherent processing and per-tensor e4m3
+// quantisation of Q, K (rotated) and V (not rotated).
+//
+// Pages cited (short names):
+//   [Evolution]  "FlashAttention evolution" (sandeep007734.github.io,
+//                posts/flashattention-evolution)
+//   [Comparison] "FlashAttention 1-4 generation comparison"
+//                (phantomic12.github.io, inference-research)
+//
+// FlashAttention-3's fp8 mode multiplies Q and K along the head dimension by
+// one random orthogonal matrix, a Hadamard matrix with random signs, before
+// quantising ([Comparison] "Notes", FA-3 entry; [Evolution] §4): Q Kᵀ is
+// unchanged and an outlier channel is spread over all d channels, so the
+// per-tensor scale loses less range.  With R = diag(signs) H_d / sqrt(d)
+// (H_d the Sylvester Hadamard matrix) this step produces
+//   u        = (x ∘ signs) · H_d          fast Walsh-Hadamard transform, fp32
+//   descale  = max|u| / (448 sqrt(d))     so that code · descale ≈ x · R
+//   code     = e4m3(448 · u / max|u|)     round to nearest even, ±448 clamp
+// and without signs u = x, descale = max|x| / 448.  The 1/sqrt(d) of R only
+// enters the reported descale: the code of an element depends on u / max|u|,
+// which the normalisation does not change.
+//
+// Two HBM-bound passes (the tensor-wide maximum sits between them):
+//   fa_fp8_absmax_d*    each workgroup transforms a grid-strided share of the
+//                       rows and writes its largest |u| to the workspace;
+//   fa_fp8_quant_d*     each workgroup reduces the workspace (all of them
+//                       alike, so no ordering between workgroups is needed),
+//                       transforms its rows again and stores the codes;
+//                       workgroup 0 writes the descale.
+// Recomputing the transform costs one more read of x (2 bytes per element)
+// instead of writing and reading an fp32 copy (8).
+//
+// Row layout: a row of d bf16 values is d/8 lanes x 16 bytes, so one wave
+// holds 64/(d/8) rows; lane j of a row holds elements 8j .. 8j+7.  The
+// transform's three low index bits are butterflies inside a lane, the
+// others butterflies between lanes j and j ^ m (shuffles within the row).
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kQuantThreads = 256;
+constexpr int kQuantMaxBlocks = 1024;
+
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+template <int D>
+struct QShape {
+  static constexpr int L = D / 8;           // lanes per row
+  static constexpr int RPW = 64 / L;        // rows per wave
+  static constexpr int RPB = RPW * (kQuantThreads / 64);   // rows per workgroup pass
+  static_assert(D == 64 || D == 128, "rotation head dims");
+};
+
+// Sign-bit masks of this lane's 8 elements (0 without rotation).
+__device__ __forceinline__ void sign_masks(const int8_t* signs, int j, unsigned (&neg)[8]) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) neg[s] = (signs && signs[8 * j + s] < 0) ? 0x80000000u : 0u;
+}
+
+// Loads this lane's 8 values of row `row` (zeros past the last row) and,
+// when `rotate`, applies the signs and the Walsh-Hadamard transform of the
+// row.
+template <int D>
+__device__ __forceinline__ void load_transform(const uint16_t* x, const unsigned (&neg)[8],
+                                               bool rotate, int row, int rows, int j,
+                                               float (&v)[8]) {
+  u16x8 w = {};
+  if (row < rows) w = *reinterpret_cast<const u16x8*>(x + (size_t)row * D + 8 * j);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) v[s] = __uint_as_float(((unsigned)w[s] << 16) ^ neg[s]);
+  if (!rotate) return;
+  // Butterflies over index bits 0..2 (inside the lane).
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if ((s & h) == 0) {
+        const float a = v[s], b = v[s + h];
+        v[s] = a + b;
+        v[s + h] = a - b;
+      }
+  // Butterflies over index bits 3.. (lane bit m of the row): the lane with
+  // the bit clear keeps a + b, its partner a - b.
+#pragma unroll
+  for (int m = 1; m < QShape<D>::L; m <<= 1) {
+    const bool upper = (j & m) != 0;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const float o = __shfl_xor(v[s], m);
+      v[s] = upper ? o - v[s] : v[s] + o;
+    }
+  }
+}
+
+__device__ __forceinline__ float block_max(float x, float* red) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = x;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kQuantThreads / 64; ++w) r = fmaxf(r, red[w]);
+  return r;
+}
+
+template <int D>
+__device__ __forceinline__ void absmax_body(const QuantParams& p) {
+  using S = QShape<D>;
+  __shared__ float red[kQuantThreads / 64];
+  const int lane = threadIdx.x & 63;
+  const int j = lane % S::L;
+  const int r_in = (threadIdx.x >> 6) * S::RPW + lane / S::L;
+  unsigned neg[8];
+  sign_masks(p.signs, j, neg);
+  float mx = 0.f;
+  for (int r0 = blockIdx.x * S::RPB; r0 < p.rows; r0 += gridDim.x * S::RPB) {
+    float v[8];
+    load_transform<D>(p.x, neg, p.signs != nullptr, r0 + r_in, p.rows, j, v);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) mx = fmaxf(mx, fabsf(v[s]));
+  }
+  mx = block_max(mx, red);
+  if (threadIdx.x == 0) p.partial[blockIdx.x] = mx;
+}
+
+template <int D>
+__device__ __forceinline__ void quant_body(const QuantParams& p) {
+  using S = QShape<D>;
+  __shared__ float red[kQuantThreads / 64];
+  float mx = 0.f;
+  for (int i = threadIdx.x; i < p.nblocks; i += kQuantThreads) mx = fmaxf(mx, p.partial[i]);
+  const float amax = block_max(mx, red);
+  const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    *p.descale = amax > 0.f ? amax / (448.0f * p.norm) : 1.0f;
+
+  const int lane = threadIdx.x & 63;
+  const int j = lane % S::L;
+  const int r_in = (threadIdx.x >> 6) * S::RPW + lane / S::L;
+  unsigned neg[8];
+  sign_masks(p.signs, j, neg);
+  for (int r0 = blockIdx.x * S::RPB; r0 < p.rows; r0 += gridDim.x * S::RPB) {
+    const int row = r0 + r_in;
+    float v[8];
+    load_transform<D>(p.x, neg, p.signs != nullptr, row, p.rows, j, v);
+    float c[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) c[s] = fminf(fmaxf(v[s] * inv, -448.0f), 448.0f);
+    // Byte t of the 8-byte group is element 8j + t.
+    unsigned lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
+    unsigned hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], hi, true);
+    if (row < p.rows) {
+      uint2 w;
+      w.x = lo;
+      w.y = hi;
+      *reinterpret_cast<uint2*>(p.codes + (size_t)row * D + 8 * j) = w;
+    }
+  }
+}
+
+}  // namespace
+}  // namespace fa
+
+#define FA_FP8_QUANT_KERNELS(D)                                                              \
+  extern "C" __global__ void __launch_bounds__(fa::kQuantThreads) fa_fp8_absmax_d##D(      \
+      fa::QuantParams p) {                                                                 \
+    fa::absmax_body<D>(p);                                                                 \
+  }                                                                                        \
+  extern "C" __global__ void __launch_bounds__(fa::kQuantThreads) fa_fp8_quant_d##D(       \
+      fa::QuantParams p) {                                                                 \
+    fa::quant_body<D>(p);                                                                  \
+  }
+
+FA_FP8_QUANT_KERNELS(64)
+FA_FP8_QUANT_KERNELS(128)
+
+namespace fa {
+
+int quant_blocks(int rows, int d) {
+  const int rpb = (64 / (d / 8)) * (kQuantThreads / 64);
+  const long long need = ((long long)rows + rpb - 1) / rpb;
+  return (int)(need < kQuantMaxBlocks ? need : kQuantMaxBlocks);
+}
+
+const char* quant_kernel_name(int d, int stage) {
+  if (d == 64) return stage == 0 ? "fa_fp8_absmax_d64" : "fa_fp8_quant_d64";
+  if (d == 128) return stage == 0 ? "fa_fp8_absmax_d128" : "fa_fp8_quant_d128";
+  return nullptr;
+}
+
+hipError_t launch_quant(const QuantParams& p, int d, hipStream_t s) {
+  const void* k0 = d == 64 ? (const void*)fa_fp8_absmax_d64 : (const void*)fa_fp8_absmax_d128;
+  const void* k1 = d == 64 ? (const void*)fa_fp8_quant_d64 : (const void*)fa_fp8_quant_d128;
+  QuantParams arg = p;
+  void* args[] = {&arg};
+  hipError_t e = hipLaunchKernel(k0, dim3(p.nblocks), dim3(kQuantThreads), args, 0, s);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel(k1, dim3(p.nblocks), dim3(kQuantThreads), args, 0, s);
+}
+
+}  // namespace fa

@@ -121,6 +121,15 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
   const int row = qw + n;
   const int off = p.Nk - p.Nq;
 
+  // Exponent factor scale * q_descale * k_descale * log2(e) and the V
+  // factor: from the arguments, or from device memory when the descales
+  // were produced on the device (the quantisation step writes them).
+  float cexp = p.c, vds = p.v_descale;
+  if (p.q_ds) {
+    cexp = p.c * *p.q_ds * *p.k_ds;
+    vds = *p.v_ds;
+  }
+
   const uint8_t* kbase = p.k + (size_t)(b * p.Hkv + g) * p.Nk * D;
   const uint8_t* vbase = p.v + (size_t)(b * p.Hkv + g) * p.Nk * D;
 
@@ -196,7 +205,7 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
     for (int kb = 0; kb < S::KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) x = fmaxf(fmaxf(x, sacc[kb][r]), sacc[kb][r + 1]);
-    return f8_half_max(x) * p.c;
+    return f8_half_max(x) * cexp;
   };
 
   auto step = [&](const lds_char* kr, const lds_char* vr, lds_char* kw, lds_char* vw,
@@ -221,10 +230,10 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         const int kb = w >> 2, r0 = 4 * (w & 3);
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 0], p.c, nm));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 1], p.c, nm));
-        const float e2 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 2], p.c, nm));
-        const float e3 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 3], p.c, nm));
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 0], cexp, nm));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 1], cexp, nm));
+        const float e2 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 2], cexp, nm));
+        const float e3 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 3], cexp, nm));
         t0 += e0 + e2;
         t1 += e1 + e3;
         int x = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
@@ -279,7 +288,7 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
 
   const float l_tot = f8_half_sum(l_run[0] + l_run[1]);
   if (row < p.Nq) {
-    const float inv = p.v_descale / l_tot;
+    const float inv = vds / l_tot;
     uint16_t* orow = p.o + ((size_t)bh * p.Nq + row) * D;
 #pragma unroll
     for (int db = 0; db < S::DB; ++db)

@@ -40,8 +40,26 @@ struct FwdF8Params {
   float* lse;
   int B, Hq, Hkv, Nq, Nk;
   int group;
-  float c;
-  float v_descale;
+  float c;           // scale * q_descale * k_descale * log2(e), or scale * log2(e)
+  float v_descale;   //   when the descales come from device memory (q_ds != null)
+  const float* q_ds;
+  const float* k_ds;
+  const float* v_ds;
+};
+
+// Arguments of one fp8 quantisation (two launches over the same rows).
+// signs: ±1 per head-dim channel (int8, negative = -1) or null for no
+// rotation; partial: one float per workgroup of the first launch; norm:
+// sqrt(d) with rotation, else 1 (divides the reported descale).
+struct QuantParams {
+  const uint16_t* x;
+  const int8_t* signs;
+  uint8_t* codes;
+  float* descale;
+  float* partial;
+  int rows;
+  int nblocks;
+  float norm;
 };
 
 // Arguments of one split-KV decode (split kernel + merge kernel).
@@ -97,6 +115,9 @@ const char* fwd_kernel_name(int d, bool causal, int Nq, int Nk);
 const char* decode_kernel_name(int d, int group, int stage);
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdF8Params& p, int d, bool causal, hipStream_t s);
+int quant_blocks(int rows, int d);
+const char* quant_kernel_name(int d, int stage);
+hipError_t launch_quant(const QuantParams& p, int d, hipStream_t s);
 const char* fwd_fp8_kernel_name(int d, bool causal);
 int fwd_fp8_rows_per_block();
 const char* bwd_kernel_name(int d, bool causal, int stage);

@@ -92,8 +92,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * fa_fwd's on those real values; inside, S = Q K^T is exact up to fp32
  * accumulation and P is rounded to e4m3 before P V, which bounds the error
  * of each output element by about 2^-4 * max|v| (plus bf16 rounding of O).
- * Incoherent processing (a random Hadamard rotation of Q and K before
- * quantisation) is the caller's preprocessing and is not applied here.
+ * Incoherent processing (the random Hadamard rotation of Q and K) happens
+ * before quantisation, in fa_fp8_quantize below; this call takes the codes.
  *
  *   q         fp8 e4m3 [B][Hq][Nq][d]
  *   k, v      fp8 e4m3 [B][Hkv][Nk][d]
@@ -107,6 +107,60 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
                float q_descale, float k_descale, float v_descale, int causal,
                void* stream);
+
+/*
+ * fa_fwd_fp8_devscale -- fa_fwd_fp8 with the three dequantisation factors
+ * read from device memory when the kernel starts (each a single fp32, as
+ * fa_fp8_quantize writes it), so that quantisation and attention run on one
+ * stream without a host round trip.  q_descale, k_descale, v_descale are
+ * device pointers (4-byte aligned, not overlapping o or lse); their values
+ * must be finite and > 0.  Other arguments and errors as fa_fwd_fp8.
+ */
+int fa_fwd_fp8_devscale(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                        const float* q_descale, const float* k_descale,
+                        const float* v_descale, int causal, void* stream);
+
+/*
+ * fa_fp8_quantize -- the fp8 input step: incoherent processing and
+ * per-tensor e4m3 quantisation ([Comparison] "Notes", FA-3 entry: FP8 with
+ * a Hadamard transform; [Evolution] §4).
+ *
+ * Q and K are rotated along the head dimension by the same random
+ * orthogonal matrix R = diag(signs) H_d / sqrt(d), H_d the Sylvester
+ * Hadamard matrix (H[i][j] = (-1)^popcount(i & j)), which leaves Q K^T
+ * unchanged and spreads one channel's outliers over all d channels; V is
+ * quantised without rotation (signs NULL).  For a tensor x of `rows` rows
+ * of d values:
+ *   y        = x R                (x without signs)
+ *   descale  = max |y| / 448      (1 when x is all zero)
+ *   codes    = e4m3(y / descale)  round to nearest, ties to even, within
+ *                                 +-448; the sign of y is kept (-0 = 0x80)
+ * so that codes * descale approximates y to 3 mantissa bits.  The rotation
+ * runs in fp32 as a fast Walsh-Hadamard transform; its 1/sqrt(d) goes into
+ * descale only.
+ *
+ *   x         bf16 [rows][d] (any [B][H][N][d] tensor: rows = B*H*N)
+ *   codes     fp8 e4m3 [rows][d]    output
+ *   descale   device fp32, 1 value  output (feed to fa_fwd_fp8_devscale)
+ *   signs     device int8 [d], negative = -1, otherwise +1; or NULL
+ *   d         64 or 128
+ *   workspace device scratch of at least fa_fp8_quantize_workspace_size(rows,
+ *             d) bytes, 16-byte aligned; its contents on entry do not matter
+ * Two kernels on `stream`: the first writes one partial maximum per
+ * workgroup into the workspace, the second reduces them and writes codes and
+ * descale.  Errors: FA_ERR_NULL, FA_ERR_SHAPE (rows <= 0), FA_ERR_HEAD_DIM,
+ * FA_ERR_ALIGN (x, codes, workspace not 16-byte or descale not 4-byte
+ * aligned), FA_ERR_WORKSPACE, FA_ERR_ALIAS (codes, descale or workspace
+ * overlapping each other, x or signs).
+ */
+size_t fa_fp8_quantize_workspace_size(int rows, int d);
+int fa_fp8_quantize(const void* x, void* codes, float* descale, const void* signs, int rows,
+                    int d, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Kernel symbol of fa_fp8_quantize: stage 0 the maximum pass, 1 the
+ * quantising pass; NULL for an unsupported d. */
+const char* fa_fp8_quantize_kernel_name(int d, int stage);
 
 /*
  * Split-KV decode ([Evolution] §6, Flash-Decoding): one query row per

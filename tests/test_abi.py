@@ -301,3 +301,53 @@ def test_fp8_rejects(kw, code):
     assert fa.fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
                          a["Nq"], a["Nk"], a["d"], a["scale"], a["qd"], a["kd"], a["vd"],
                          a["causal"], None) == code
+
+
+def test_quantize_names_and_workspace():
+    assert fa.fa_fp8_quantize_kernel_name(128, 0) == "fa_fp8_absmax_d128"
+    assert fa.fa_fp8_quantize_kernel_name(64, 1) == "fa_fp8_quant_d64"
+    assert fa.fa_fp8_quantize_kernel_name(32, 0) is None
+    assert fa.fa_fp8_quantize_kernel_name(128, 2) is None
+    # One float per workgroup of the first pass: 16 rows (d = 128) or 32
+    # rows (d = 64) per workgroup, at most 1024 workgroups.
+    assert fa.fa_fp8_quantize_workspace_size(1, 128) == 4
+    assert fa.fa_fp8_quantize_workspace_size(17, 128) == 8
+    assert fa.fa_fp8_quantize_workspace_size(33, 64) == 8
+    assert fa.fa_fp8_quantize_workspace_size(32 * 16384, 128) == 4096
+    assert fa.fa_fp8_quantize_workspace_size(0, 128) == 0
+    assert fa.fa_fp8_quantize_workspace_size(16, 256) == 0
+
+
+S8 = 0x700000   # placeholder address of the signs vector
+DS = 0x800000   # placeholder address of the descale output
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=0), -1), (dict(codes=0), -1), (dict(ds=0), -1),
+    (dict(rows=0), -2), (dict(rows=-5), -2), (dict(d=32), -3), (dict(d=256), -3),
+    (dict(x=Q + 8), -4), (dict(codes=O + 4), -4), (dict(ds=DS + 2), -4),
+    (dict(ws=0), -5), (dict(wsb=4), -5), (dict(ws=W + 4), -4),
+    (dict(codes=Q + 64), -9), (dict(ds=Q + 16), -9), (dict(ws=O), -9),
+    (dict(ds=W), -9), (dict(codes=S8 - 64), -9),
+])
+def test_quantize_rejects(kw, code):
+    a = dict(x=Q, codes=O, ds=DS, signs=S8, rows=1000, d=128, ws=W, wsb=1 << 20)
+    a.update(kw)
+    assert fa.fa_fp8_quantize(a["x"], a["codes"], a["ds"], a["signs"], a["rows"], a["d"],
+                              a["ws"], a["wsb"], None) == code
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(qd=0), -1), (dict(vd=0), -1), (dict(q=0), -1), (dict(d=32), -3),
+    (dict(scale=0.0), -8), (dict(kd=DS + 2), -4), (dict(qd=O + 64), -9), (dict(vd=L), -9),
+    (dict(B=0), -2),
+])
+def test_fp8_devscale_rejects(kw, code):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, Hq=4, Hkv=2, Nq=64, Nk=64, d=128, scale=0.125,
+             qd=DS, kd=DS + 4, vd=DS + 8, causal=1)
+    a.update(kw)
+    assert fa.fa_fwd_fp8_devscale(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                                  a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"], a["qd"],
+                                  a["kd"], a["vd"], a["causal"], None) == code
