@@ -169,7 +169,56 @@ def fp8_leg(fa, cfg, stream, steps, warmup=20):
             "kernel": kname,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
-                         "traffic": _traffic(kname, srcs)}}
+                         "traffic": _traffic(kname, srcs)},
+            "quantize": quantize_leg(fa, cfg, stream, steps)}
+
+
+def quantize_leg(fa, cfg, stream, steps, warmup=20):
+    """fa_fp8_quantize of the prefill's bf16 Q (rotated), K (rotated) and V
+    (not rotated), timed per call; GB/s over the algorithmic 3 bytes per
+    element (read bf16, write the e4m3 code)."""
+    import torch
+    qb, kb, vb = datagen.make_fwd_inputs(cfg)
+    xs = [_dev(x) for x in (qb, kb, vb)]
+    signs = torch.from_numpy(datagen.random_signs(cfg.seed, cfg.d)).to("cuda:0")
+    rows = [x.numel() // cfg.d for x in xs]
+    codes = [torch.empty(x.shape, dtype=torch.uint8, device="cuda") for x in xs]
+    ds = torch.empty(3, dtype=torch.float32, device="cuda")
+    wss = [torch.empty(fa.fa_fp8_quantize_workspace_size(r, cfg.d), dtype=torch.uint8,
+                       device="cuda") for r in rows]
+    sp = stream.cuda_stream
+
+    def call(i):
+        rc = fa.fa_fp8_quantize(xs[i].data_ptr(), codes[i].data_ptr(), ds[i:].data_ptr(),
+                                signs.data_ptr() if i < 2 else None, rows[i], cfg.d,
+                                wss[i].data_ptr(), wss[i].numel(), sp)
+        if rc:
+            raise fa.FAError(rc, "fa_fp8_quantize")
+
+    for _ in range(warmup):
+        for i in range(3):
+            call(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in evs:
+        e[0].record(stream)
+        call(0)
+        e[1].record(stream)
+        call(1)
+        call(2)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    nbytes = 3 * xs[0].numel()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"tensor": f"Q [{cfg.B}][{cfg.Hq}][{cfg.Nq}][{cfg.d}] bf16, rotated",
+            "ms": round(ms, 4), "value": round(gbs, 1), "unit": "GB/s",
+            "kernels": [fa.fa_fp8_quantize_kernel_name(cfg.d, 0),
+                        fa.fa_fp8_quantize_kernel_name(cfg.d, 1)],
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": _traffic(f"fa_fp8_quantize_d{cfg.d}",
+                                             ["exact_attention_103_amd/csrc/fa_fp8_quant.hip",
+                                              "exact_attention_103_amd/csrc/fa_internal.h"])}}
 
 
 def bwd_leg(fa, cfg, q, k, v, o, lse, stream, steps, warmup=10):

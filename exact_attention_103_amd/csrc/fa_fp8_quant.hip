@@ -33,7 +33,8 @@
 // Row layout: a row of d bf16 values is d/8 lanes x 16 bytes, so one wave
 // holds 64/(d/8) rows; lane j of a row holds elements 8j .. 8j+7.  The
 // transform's three low index bits are butterflies inside a lane, the
-// others butterflies between lanes j and j ^ m (shuffles within the row).
+// others butterflies between lanes j and j ^ m, exchanged with DPP moves
+// inside the 16-lane rows of the wave (a row of d = 128 is one DPP row).
 
 #include "fa_internal.h"
 
@@ -59,15 +60,54 @@ __device__ __forceinline__ void sign_masks(const int8_t* signs, int j, unsigned 
   for (int s = 0; s < 8; ++s) neg[s] = (signs && signs[8 * j + s] < 0) ? 0x80000000u : 0u;
 }
 
-// Loads this lane's 8 values of row `row` (zeros past the last row) and,
-// when `rotate`, applies the signs and the Walsh-Hadamard transform of the
-// row.
+// x from lane i ^ M within the 16-lane DPP row, as VALU moves (no LDS):
+// M = 1, 2 are quad permutations; M = 4 is the quad permutation i ^ 3
+// followed by the half-row mirror (i ^ 7); M = 8 the half-row mirror
+// followed by the row mirror (i ^ 15).
+template <int M>
+__device__ __forceinline__ float lane_xor(float x) {
+  const int v = __float_as_int(x);
+  constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kQuadXor3 = 0x1B;
+  constexpr int kRowMirror = 0x140, kHalfMirror = 0x141;
+  int r;
+  if constexpr (M == 1) {
+    r = __builtin_amdgcn_mov_dpp(v, kQuadXor1, 0xF, 0xF, true);
+  } else if constexpr (M == 2) {
+    r = __builtin_amdgcn_mov_dpp(v, kQuadXor2, 0xF, 0xF, true);
+  } else if constexpr (M == 4) {
+    r = __builtin_amdgcn_mov_dpp(v, kQuadXor3, 0xF, 0xF, true);
+    r = __builtin_amdgcn_mov_dpp(r, kHalfMirror, 0xF, 0xF, true);
+  } else {
+    static_assert(M == 8, "lane distance within a 16-lane row");
+    r = __builtin_amdgcn_mov_dpp(v, kHalfMirror, 0xF, 0xF, true);
+    r = __builtin_amdgcn_mov_dpp(r, kRowMirror, 0xF, 0xF, true);
+  }
+  return __int_as_float(r);
+}
+
+// One butterfly stage between lanes j and j ^ M: the lane with bit M clear
+// keeps a + b, its partner a - b, i.e. partner's value + (+-1) * own value
+// (one exact FMA: the product by +-1 does not round).
+template <int M>
+__device__ __forceinline__ void lane_butterfly(float (&v)[8], int j) {
+  const float sgn = (j & M) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) v[s] = fmaf(sgn, v[s], lane_xor<M>(v[s]));
+}
+
+// This lane's 16 bytes of row `row` (zeros past the last row).
 template <int D>
-__device__ __forceinline__ void load_transform(const uint16_t* x, const unsigned (&neg)[8],
-                                               bool rotate, int row, int rows, int j,
-                                               float (&v)[8]) {
+__device__ __forceinline__ u16x8 load_row(const uint16_t* x, int row, int rows, int j) {
   u16x8 w = {};
   if (row < rows) w = *reinterpret_cast<const u16x8*>(x + (size_t)row * D + 8 * j);
+  return w;
+}
+
+// The lane's 8 values as fp32 and, when `rotate`, with the signs applied
+// and the Walsh-Hadamard transform of the row.
+template <int D>
+__device__ __forceinline__ void transform(u16x8 w, const unsigned (&neg)[8], bool rotate, int j,
+                                          float (&v)[8]) {
 #pragma unroll
   for (int s = 0; s < 8; ++s) v[s] = __uint_as_float(((unsigned)w[s] << 16) ^ neg[s]);
   if (!rotate) return;
@@ -81,18 +121,17 @@ __device__ __forceinline__ void load_transform(const uint16_t* x, const unsigned
         v[s] = a + b;
         v[s + h] = a - b;
       }
-  // Butterflies over index bits 3.. (lane bit m of the row): the lane with
-  // the bit clear keeps a + b, its partner a - b.
-#pragma unroll
-  for (int m = 1; m < QShape<D>::L; m <<= 1) {
-    const bool upper = (j & m) != 0;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const float o = __shfl_xor(v[s], m);
-      v[s] = upper ? o - v[s] : v[s] + o;
-    }
-  }
+  // Butterflies over index bits 3.. (lane bit m of the row).
+  lane_butterfly<1>(v, j);
+  lane_butterfly<2>(v, j);
+  lane_butterfly<4>(v, j);
+  if constexpr (QShape<D>::L == 16) lane_butterfly<8>(v, j);
 }
+
+// Rows are visited in steps of kQuantUnroll row groups per workgroup, whose
+// loads are all issued before the first transform (more bytes in flight per
+// wave).
+constexpr int kQuantUnroll = 4;
 
 __device__ __forceinline__ float block_max(float x, float* red) {
 #pragma unroll
@@ -116,11 +155,18 @@ __device__ __forceinline__ void absmax_body(const QuantParams& p) {
   unsigned neg[8];
   sign_masks(p.signs, j, neg);
   float mx = 0.f;
-  for (int r0 = blockIdx.x * S::RPB; r0 < p.rows; r0 += gridDim.x * S::RPB) {
-    float v[8];
-    load_transform<D>(p.x, neg, p.signs != nullptr, r0 + r_in, p.rows, j, v);
+  const int stride = gridDim.x * S::RPB;
+  for (int r0 = blockIdx.x * S::RPB; r0 < p.rows; r0 += kQuantUnroll * stride) {
+    u16x8 w[kQuantUnroll];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) mx = fmaxf(mx, fabsf(v[s]));
+    for (int u = 0; u < kQuantUnroll; ++u) w[u] = load_row<D>(p.x, r0 + u * stride + r_in, p.rows, j);
+#pragma unroll
+    for (int u = 0; u < kQuantUnroll; ++u) {
+      float v[8];
+      transform<D>(w[u], neg, p.signs != nullptr, j, v);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) mx = fmaxf(mx, fabsf(v[s]));
+    }
   }
   mx = block_max(mx, red);
   if (threadIdx.x == 0) p.partial[blockIdx.x] = mx;
@@ -142,23 +188,30 @@ __device__ __forceinline__ void quant_body(const QuantParams& p) {
   const int r_in = (threadIdx.x >> 6) * S::RPW + lane / S::L;
   unsigned neg[8];
   sign_masks(p.signs, j, neg);
-  for (int r0 = blockIdx.x * S::RPB; r0 < p.rows; r0 += gridDim.x * S::RPB) {
-    const int row = r0 + r_in;
-    float v[8];
-    load_transform<D>(p.x, neg, p.signs != nullptr, row, p.rows, j, v);
-    float c[8];
+  const int stride = gridDim.x * S::RPB;
+  for (int r0 = blockIdx.x * S::RPB; r0 < p.rows; r0 += kQuantUnroll * stride) {
+    u16x8 w[kQuantUnroll];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) c[s] = fminf(fmaxf(v[s] * inv, -448.0f), 448.0f);
-    // Byte t of the 8-byte group is element 8j + t.
-    unsigned lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
-    unsigned hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], hi, true);
-    if (row < p.rows) {
-      uint2 w;
-      w.x = lo;
-      w.y = hi;
-      *reinterpret_cast<uint2*>(p.codes + (size_t)row * D + 8 * j) = w;
+    for (int u = 0; u < kQuantUnroll; ++u) w[u] = load_row<D>(p.x, r0 + u * stride + r_in, p.rows, j);
+#pragma unroll
+    for (int u = 0; u < kQuantUnroll; ++u) {
+      const int row = r0 + u * stride + r_in;
+      float v[8];
+      transform<D>(w[u], neg, p.signs != nullptr, j, v);
+      float c[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) c[s] = fminf(fmaxf(v[s] * inv, -448.0f), 448.0f);
+      // Byte t of the 8-byte group is element 8j + t.
+      unsigned lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
+      unsigned hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], hi, true);
+      if (row < p.rows) {
+        uint2 o;
+        o.x = lo;
+        o.y = hi;
+        *reinterpret_cast<uint2*>(p.codes + (size_t)row * D + 8 * j) = o;
+      }
     }
   }
 }

@@ -6,7 +6,7 @@ Prints one JSON line per workload: the kernel that ran, the median launch
 time (HIP events on the launch stream) and TFLOP/s for the forward (flop =
 4*B*H*Nq*Nk*d, halved when causal) or GB/s for the decode (K + V cache read
 once, plus q, O and LSE; for the serving decode only each sequence's first
-seqlens[b] keys count).  Inputs are random bf16 tensors of the workload's
+seqlens[b] keys count; for the fp8 quantisation 3 bytes per element).  Inputs are random bf16 tensors of the workload's
 shape and scaling; the forward's speed does not depend on the values.
 """
 
@@ -95,6 +95,27 @@ def main():
                           "ms": round(ms, 4), "tflops": round(flop / ms / 1e9, 1),
                           "pct_of_5000": round(100 * flop / ms / 1e9 / 5000, 1)}), flush=True)
         del q8, k8, v8, o, lse
+    for name, B, H, N, d in (("long", 1, 32, 16384, 128), ("train", 8, 16, 2048, 128),
+                             ("sweep_d64", 2, 16, 4096, 64)):
+        # fp8 input step on one bf16 tensor: rotated (Q, K) and plain (V);
+        # GB/s over 3 bytes per element (bf16 read, e4m3 code written).
+        x = torch.randn(B, H, N, d, device="cuda").to(torch.bfloat16)
+        signs = torch.where(torch.rand(d, device="cuda") < 0.5, -1, 1).to(torch.int8)
+        codes = torch.empty(x.shape, dtype=torch.uint8, device="cuda")
+        dsc = torch.empty(1, dtype=torch.float32, device="cuda")
+        ws = torch.empty(fa.fa_fp8_quantize_workspace_size(B * H * N, d), dtype=torch.uint8,
+                         device="cuda")
+        for rot in (True, False):
+            ms = _time(lambda: fa.fp8_quantize(x, signs if rot else None, codes, dsc, ws),
+                       args.iters, args.warmup)
+            nbytes = 3 * x.numel()
+            print(json.dumps({"workload": name + "_quantize", "B": B, "H": H, "N": N, "d": d,
+                              "rotated": rot, "kernels": [fa.fa_fp8_quantize_kernel_name(d, 0),
+                                                          fa.fa_fp8_quantize_kernel_name(d, 1)],
+                              "ms": round(ms, 4), "gbs": round(nbytes / ms / 1e6, 1),
+                              "pct_of_8000": round(100 * nbytes / ms / 1e6 / 8000, 1)}),
+                  flush=True)
+        del x, codes, ws
     for B, Hq, Hkv, Nk, d, S in DECODE:
         q = torch.randn(B, Hq, d, device="cuda").to(torch.bfloat16)
         kc = torch.randn(B, Hkv, Nk, d, device="cuda").to(torch.bfloat16)
