@@ -48,6 +48,8 @@ ODD = [
     (1, 1, 1, 1, 1, 128, False),
     (1, 2, 1, 3, 700, 128, True),
     (1, 8, 8, 129, 129, 128, True),
+    (1, 8, 1, 150, 150, 64, False),   # eight query heads per KV head
+    (2, 16, 2, 97, 161, 128, True),   # GQA 8, Nq < Nk, ragged in both
 ]
 
 
