@@ -151,19 +151,24 @@ __device__ __forceinline__ void decode_split_body(const DecodeParams& p, lds_cha
   // Issue the loads of this wave's i-th tile: K rows into registers (A
   // operand layout: lane (grp, col) takes key col, d = 32t + 8grp ..), V rows
   // into LDS.  Keys past the chunk end re-read its last key (masked later).
+  // Every K/V byte is read once, so both loads are nontemporal (the `nt`
+  // cache policy): a 1 GiB streaming read measured 6.8 TB/s with it against
+  // 6.2 without.
   auto issue = [&](int i, bf16x8 (&kf)[S::KSTEPS], lds_char* vt) {
     const int tb = kbeg + kDecTile * (wave + kDecWaves * i);
     const int key = min(tb + col, kend - 1);
 #pragma unroll
     for (int t = 0; t < S::KSTEPS; ++t)
-      kf[t] = *reinterpret_cast<const bf16x8*>(kb + (size_t)key * D + 32 * t + 8 * grp);
+      kf[t] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                                             kb + (size_t)key * D + 32 * t + 8 * grp)));
 #pragma unroll
     for (int L = 0; L < S::VLOADS; ++L) {
       const int P = L * 64 + lane;
       const int row = P / S::CPR;
       const int c = (P % S::CPR) ^ dv_xor<S::RB>(row);
       const int vkey = min(tb + row, kend - 1);
-      __builtin_amdgcn_global_load_lds(vb + (size_t)vkey * D + c * 8, vt + L * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vb + (size_t)vkey * D + c * 8, vt + L * 1024, 16, 0,
+                                       kCachePolicyNT);
     }
   };
 

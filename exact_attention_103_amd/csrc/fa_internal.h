@@ -12,6 +12,12 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Cache-policy operand of __builtin_amdgcn_global_load_lds for a
+// nontemporal (streaming) load: the `nt` bit of gfx950's global loads.
+constexpr int kCachePolicyNT = 2;
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
