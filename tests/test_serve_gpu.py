@@ -101,6 +101,19 @@ def test_serve_workload(splits):
     _check(f"serve workload S={splits}", qb, kb, vb, lens, cfg.scale, cfg.causal, splits)
 
 
+@pytest.mark.parametrize("splits", [0, 3, 16])
+def test_serve_skewed_lengths(splits):
+    """One full-capacity sequence next to short ones (and one of a single
+    key): the long sequence's chunks are many times the short ones'."""
+    B, Hq, Hkv, Nq, Nk, d = 8, 8, 2, 3, 4096, 128
+    tag = f"serve skewed lengths S={splits}"
+    announce(tag)
+    lens = np.array([4096, 64, 65, 1, 100, 3000, 64, 129], np.int32)
+    qb, kb, vb = datagen.gaussian_bf16(950 + splits, [(B, Hq, Nq, d), (B, Hkv, Nk, d),
+                                                      (B, Hkv, Nk, d)])
+    _check(tag, qb, kb, vb, lens, 1 / np.sqrt(d), True, splits)
+
+
 def test_serve_matches_plain_decode_bitwise():
     """One row per sequence and no length array is the plain split-KV decode:
     same partition, same arithmetic, identical bits."""
