@@ -24,10 +24,13 @@ __all__ = [
     "fa_fwd_fp8_devscale", "fa_fp8_quantize", "fa_fp8_quantize_workspace_size",
     "fa_fp8_quantize_kernel_name",
     "fwd", "fwd_fp8", "fp8_quantize", "decode", "decode_serve", "bwd", "EXPORTED_SYMBOLS",
-    "LIB_PATH",
+    "LIB_PATH", "SERIAL_LIB_PATH", "load_library",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+# Race-check build of the same sources (staged copies never overlap compute);
+# only tests load it.
+SERIAL_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_serial.so")
 
 FA_OK = 0
 
@@ -83,20 +86,26 @@ class FAError(RuntimeError):
         self.status = status
 
 
+def load_library(path=LIB_PATH):
+    """Open a build of the C ABI (libfa.so, or the race-check build
+    libfa_serial.so) with every declared signature set.  Raises if the file
+    has not been built."""
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m exact_attention_103_amd.build`")
+    L = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
 def lib():
-    """Load libfa.so (built in-tree).  Raises if it has not been built."""
+    """The loaded libfa.so (built in-tree).  Raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(
-                f"{LIB_PATH} is missing: build it with "
-                "`python -m exact_attention_103_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in _SIGNATURES.items():
-            fn = getattr(L, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = L
+        _lib = load_library(LIB_PATH)
     return _lib
 
 

@@ -237,10 +237,12 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, lds_char* kb0, l
 
   auto step = [&](const lds_char* kr, const lds_char* vr, lds_char* kw, lds_char* vw, int j) {
     const int j0 = j * BN;
+    FA_STAGE_FENCE();
     if (j + 1 < nkt) {
       dma_rows<D, BN>(kbase, j0 + BN, p.Nk, kw, wave, lane);
       dma_rows<D, BN>(vbase, j0 + BN, p.Nk, vw, wave, lane);
     }
+    FA_STAGE_FENCE();
     f32x16 sacc[KB], dpacc[KB];
     xt_tile(kr, qf, sacc);    // S^T  = K Q^T
     xt_tile(vr, df, dpacc);   // dP^T = V dO^T
@@ -392,7 +394,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* qt0,
 
   auto step = [&](const lds_char* qt, const lds_char* dt, const lds_char* st, lds_char* qw,
                   lds_char* dw, lds_char* sw, int s) {
+    FA_STAGE_FENCE();
     if (s + 1 < steps) load(s + 1, qw, dw, sw);
+    FA_STAGE_FENCE();
     const int i0 = tile_row(s);
     const __attribute__((address_space(3))) f32x4* lse4 =
         (const __attribute__((address_space(3))) f32x4*)st;

@@ -155,6 +155,7 @@ __device__ __forceinline__ void decode_split_body(const DecodeParams& p, lds_cha
   // cache policy): a 1 GiB streaming read measured 6.8 TB/s with it against
   // 6.2 without.
   auto issue = [&](int i, bf16x8 (&kf)[S::KSTEPS], lds_char* vt) {
+    FA_STAGE_WAIT();
     const int tb = kbeg + kDecTile * (wave + kDecWaves * i);
     const int key = min(tb + col, kend - 1);
 #pragma unroll
@@ -170,6 +171,7 @@ __device__ __forceinline__ void decode_split_body(const DecodeParams& p, lds_cha
       __builtin_amdgcn_global_load_lds(vb + (size_t)vkey * D + c * 8, vt + L * 1024, 16, 0,
                                        kCachePolicyNT);
     }
+    FA_STAGE_WAIT();
   };
 
   float m = -1e30f;   // running max (base 2) of query h0+col, same in all lane groups

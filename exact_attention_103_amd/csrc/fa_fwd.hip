@@ -286,8 +286,10 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
         m_run[qb] = m_new[qb];
       }
     }
+    FA_STAGE_FENCE();
     if (j + 2 < nkt) load_tile<D, BN, NW, false>(kbase, j0 + 2 * BN, p.Nk, kw, wave, lane);
     if (j + 1 < nkt) load_tile<D, BN, NW, true>(vbase, j0 + BN, p.Nk, vw, wave, lane);
+    FA_STAGE_FENCE();
 
     // S^T of tile j+1 (its result is unused after the last tile).  With one
     // 64-key block of 32 rows per wave it is issued first and overlaps tile

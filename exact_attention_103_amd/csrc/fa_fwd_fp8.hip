@@ -212,8 +212,10 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
                   f32x16 (&sc)[S::KB], f32x16 (&sn)[S::KB], int j) {
     const int j0 = j * BN;
     if (needs_mask(j)) mask_tile(sc, j);
+    FA_STAGE_FENCE();
     if (j + 2 < nkt) f8_load_tile<D, NW>(kbase, j0 + 2 * BN, p.Nk, kw, wave, lane);
     if (j + 1 < nkt) f8_load_tile<D, NW>(vbase, j0 + BN, p.Nk, vw, wave, lane);
+    FA_STAGE_FENCE();
 
     // S^T of tile j+1 on the MFMA pipe next to tile j's softmax.
     s_tile(kr, sn);

@@ -18,6 +18,32 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 // nontemporal (streaming) load: the `nt` bit of gfx950's global loads.
 constexpr int kCachePolicyNT = 2;
 
+// Race-check build (compiled with -DFA_SERIAL_PIPELINE into a second
+// library).  Around every staged copy into LDS, FA_STAGE_FENCE waits for all
+// of the wave's outstanding memory operations and then for every wave of the
+// workgroup, on both sides of the copy; FA_STAGE_WAIT does the same for
+// copies into a wave's own LDS buffers, without the workgroup barrier.  No
+// copy then overlaps a read of the buffer it targets, nor any compute.  The
+// arithmetic and its order do not change, so that build must reproduce the
+// pipelined one bit for bit: a difference is a race between a staged copy
+// and the reads of its buffer.  FA_STAGE_FENCE is only placed where every
+// wave of the workgroup arrives.
+#ifdef FA_SERIAL_PIPELINE
+#define FA_STAGE_FENCE()                 \
+  do {                                   \
+    __builtin_amdgcn_s_waitcnt(0);       \
+    __syncthreads();                     \
+  } while (0)
+#define FA_STAGE_WAIT() __builtin_amdgcn_s_waitcnt(0)
+#else
+#define FA_STAGE_FENCE() \
+  do {                   \
+  } while (0)
+#define FA_STAGE_WAIT() \
+  do {                  \
+  } while (0)
+#endif
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

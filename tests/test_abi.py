@@ -50,6 +50,16 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), f"libfa.so does not export {name}"
 
 
+def test_serial_build_exports_every_declared_symbol():
+    # The race-check build (staged copies never overlap compute) must offer
+    # the same entry points, so the race tests can call it the same way.
+    assert os.path.exists(fa.SERIAL_LIB_PATH), "libfa_serial.so not built"
+    L = fa.load_library(fa.SERIAL_LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(L, name), f"libfa_serial.so does not export {name}"
+    assert L.fa_fwd_kernel_name(128, 1, 16384, 16384) == b"fa_fwd_d128_causal"
+
+
 def test_status_enum_matches_header():
     text = open(HEADER).read()
     codes = dict((k, int(v)) for k, v in re.findall(r"(FA_[A-Z_]+)\s*=\s*(-?\d+)", text))
