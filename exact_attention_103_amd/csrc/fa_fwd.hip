@@ -127,7 +127,7 @@ __device__ __forceinline__ void load_tile(const uint16_t* base, int j0, int Nk, 
   }
 }
 
-template <int D, int BN, int NW, int NQB, bool CAUSAL>
+template <int D, int BN, int NW, int NQB, bool CAUSAL, bool SKIP_IDLE>
 __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_char* kb1,
                                          lds_char* vb0, lds_char* vb1) {
   using S = FwdShape<D, BN, NW, NQB>;
@@ -255,9 +255,8 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
   // prefetches K_{j+2} into kw and V_{j+1} into vw, computes S^T of tile j+1
   // into sn on the MFMA pipe while the VALU turns tile j's scores into
   // probabilities and adds P_j V_j, and ends with the row maximum of tile
-  // j+1, which overlaps the last PV products.  Tiles a wave does not need
-  // (past its diagonal, or past Nk) are fully masked, so all waves run the
-  // same schedule.
+  // j+1, which overlaps the last PV products.  Keys a wave's rows may not see
+  // inside a tile it needs (past its diagonal, or past Nk) are masked.
   float mnext[NQB];
   auto step = [&](const lds_char* kr, const lds_char* vr, lds_char* kw, lds_char* vw,
                   f32x16 (&sc)[NQB][S::KB], f32x16 (&sn)[NQB][S::KB], int j) {
@@ -348,14 +347,35 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
   s_tile(kb0, sa);
   tile_max(sa, mnext);
   __syncthreads();
-  for (int j = 0; j < nkt; j += 2) {
+  // When causal, this wave's rows see only the first nkt_w tiles; later tiles
+  // would get probability exactly 0 for all of them.  With SKIP_IDLE the wave
+  // skips their products and softmax and only takes part in their copies and
+  // barriers (step j writes K_{j+2} over K_j's buffer and V_{j+1} over
+  // V_{j-1}'s); the outputs are the same bits either way.  Whether it pays
+  // depends on how the compiler then schedules the main loop, so the tile
+  // table switches it per head dim.
+  const int nkt_w = (CAUSAL && SKIP_IDLE) ? min(nkt, (qw + S::RPW - 1 + off) / BN + 1) : nkt;
+  for (int j = 0; j < nkt_w; j += 2) {
     if constexpr (kPipe) {
       step(kb1, vb0, kb0, vb1, sa, sb, j);
-      if (j + 1 < nkt) step(kb0, vb1, kb1, vb0, sb, sa, j + 1);
+      if (j + 1 < nkt_w) step(kb0, vb1, kb1, vb0, sb, sa, j + 1);
     } else {
       step(kb1, vb0, kb0, vb1, sa, sa, j);
-      if (j + 1 < nkt) step(kb0, vb1, kb1, vb0, sa, sa, j + 1);
+      if (j + 1 < nkt_w) step(kb0, vb1, kb1, vb0, sa, sa, j + 1);
     }
+  }
+  auto idle_step = [&](lds_char* kw, lds_char* vw, int j) {
+    FA_STAGE_FENCE();
+    if (j + 2 < nkt) load_tile<D, BN, NW, false>(kbase, (j + 2) * BN, p.Nk, kw, wave, lane);
+    if (j + 1 < nkt) load_tile<D, BN, NW, true>(vbase, (j + 1) * BN, p.Nk, vw, wave, lane);
+    FA_STAGE_FENCE();
+    __syncthreads();
+  };
+  int j = nkt_w;
+  if (j < nkt && (j & 1)) idle_step(kb1, vb0, j++);
+  for (; j < nkt; j += 2) {
+    idle_step(kb0, vb1, j);
+    if (j + 1 < nkt) idle_step(kb1, vb0, j + 1);
   }
 
   // Epilogue: O = acc / l (bf16, round to nearest even), LSE in natural log.
@@ -387,7 +407,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
 
 // Kernel symbols carry plain C names so that a profiler trace names exactly
 // which variant ran.
-#define FA_FWD_KERNEL(NAME, D, BN, NW, NQB, CAUSAL, WAVES_PER_EU)                    \
+#define FA_FWD_KERNEL(NAME, D, BN, NW, NQB, CAUSAL, WAVES_PER_EU, SKIP_IDLE)         \
   extern "C" __global__ void __launch_bounds__(64 * NW, WAVES_PER_EU) NAME(           \
       fa::FwdParams p) {                                                              \
     using Sh = fa::FwdShape<D, BN, NW, NQB>;                                          \
@@ -395,24 +415,26 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
     __shared__ __attribute__((aligned(1024))) char k1[Sh::TILE];                      \
     __shared__ __attribute__((aligned(1024))) char v0[Sh::TILE];                      \
     __shared__ __attribute__((aligned(1024))) char v1[Sh::TILE];                      \
-    fa::fwd_body<D, BN, NW, NQB, CAUSAL>(p, (fa::lds_char*)k0, (fa::lds_char*)k1,     \
-                                         (fa::lds_char*)v0, (fa::lds_char*)v1);       \
+    fa::fwd_body<D, BN, NW, NQB, CAUSAL, SKIP_IDLE>(p, (fa::lds_char*)k0,              \
+        (fa::lds_char*)k1, (fa::lds_char*)v0, (fa::lds_char*)v1);                     \
   }
 
 // Tile table (head dim: keys per tile, waves, query blocks of 32 rows per
-// wave, waves per SIMD).  It must match fwd_tile() below.  d = 128 has a
-// 256-row tile (8 waves share each K/V tile, for long key ranges) and a
-// 128-row tile (more workgroups per CU, for short ones).
-FA_FWD_KERNEL(fa_fwd_d32_nomask, 32, 128, 4, 1, false, 2)
-FA_FWD_KERNEL(fa_fwd_d32_causal, 32, 128, 4, 1, true, 2)
-FA_FWD_KERNEL(fa_fwd_d64_nomask, 64, 64, 4, 1, false, 2)
-FA_FWD_KERNEL(fa_fwd_d64_causal, 64, 64, 4, 1, true, 2)
-FA_FWD_KERNEL(fa_fwd_d128_nomask, 128, 64, 8, 1, false, 2)
-FA_FWD_KERNEL(fa_fwd_d128_causal, 128, 64, 8, 1, true, 2)
-FA_FWD_KERNEL(fa_fwd_d128_nomask_bm128, 128, 64, 4, 1, false, 2)
-FA_FWD_KERNEL(fa_fwd_d128_causal_bm128, 128, 64, 4, 1, true, 2)
-FA_FWD_KERNEL(fa_fwd_d256_nomask, 256, 32, 4, 1, false, 1)
-FA_FWD_KERNEL(fa_fwd_d256_causal, 256, 32, 4, 1, true, 1)
+// wave, waves per SIMD, causal idle-tile skip).  It must match fwd_tile()
+// below.  d = 128 has a 256-row tile (8 waves share each K/V tile, for long
+// key ranges) and a 128-row tile (more workgroups per CU, for short ones).
+// The idle-tile skip measured +0.4% (d = 128, 16k keys), +2% (d = 128, 2k
+// keys) and +3% (d = 32) but -3% at d = 64 and -0.3% at d = 256.
+FA_FWD_KERNEL(fa_fwd_d32_nomask, 32, 128, 4, 1, false, 2, false)
+FA_FWD_KERNEL(fa_fwd_d32_causal, 32, 128, 4, 1, true, 2, true)
+FA_FWD_KERNEL(fa_fwd_d64_nomask, 64, 64, 4, 1, false, 2, false)
+FA_FWD_KERNEL(fa_fwd_d64_causal, 64, 64, 4, 1, true, 2, false)
+FA_FWD_KERNEL(fa_fwd_d128_nomask, 128, 64, 8, 1, false, 2, false)
+FA_FWD_KERNEL(fa_fwd_d128_causal, 128, 64, 8, 1, true, 2, true)
+FA_FWD_KERNEL(fa_fwd_d128_nomask_bm128, 128, 64, 4, 1, false, 2, false)
+FA_FWD_KERNEL(fa_fwd_d128_causal_bm128, 128, 64, 4, 1, true, 2, true)
+FA_FWD_KERNEL(fa_fwd_d256_nomask, 256, 32, 4, 1, false, 1, false)
+FA_FWD_KERNEL(fa_fwd_d256_causal, 256, 32, 4, 1, true, 1, false)
 
 namespace fa {
 namespace {
