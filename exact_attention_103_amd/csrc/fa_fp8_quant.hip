@@ -30,11 +30,14 @@
 // Recomputing the transform costs one more read of x (2 bytes per element)
 // instead of writing and reading an fp32 copy (8).
 //
-// Row layout: a row of d bf16 values is d/8 lanes x 16 bytes, so one wave
-// holds 64/(d/8) rows; lane j of a row holds elements 8j .. 8j+7.  The
-// transform's three low index bits are butterflies inside a lane, the
-// others butterflies between lanes j and j ^ m, exchanged with DPP moves
-// inside the 16-lane rows of the wave (a row of d = 128 is one DPP row).
+// Row layout: a row of d bf16 values is d/16 lanes x 32 bytes, so one wave
+// holds 64/(d/16) rows; lane j of a row holds elements 16j .. 16j+15.  The
+// transform's four low index bits are butterflies inside a lane (one add or
+// subtract per element each), the others butterflies between lanes j and
+// j ^ m, exchanged with DPP moves inside the 16-lane rows of the wave (a row
+// of d = 128 is half a DPP row).  Sixteen elements per lane keep one more
+// stage inside the lane than eight would, and drop the lane distance 8,
+// whose exchange takes two DPP moves.
 
 #include "fa_internal.h"
 
@@ -48,39 +51,35 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 
 template <int D>
 struct QShape {
-  static constexpr int L = D / 8;           // lanes per row
+  static constexpr int L = D / 16;          // lanes per row
   static constexpr int RPW = 64 / L;        // rows per wave
   static constexpr int RPB = RPW * (kQuantThreads / 64);   // rows per workgroup pass
   static_assert(D == 64 || D == 128, "rotation head dims");
 };
 
-// Sign-bit masks of this lane's 8 elements (0 without rotation).
-__device__ __forceinline__ void sign_masks(const int8_t* signs, int j, unsigned (&neg)[8]) {
+// Sign-bit masks of this lane's 16 elements (0 without rotation).
+__device__ __forceinline__ void sign_masks(const int8_t* signs, int j, unsigned (&neg)[16]) {
 #pragma unroll
-  for (int s = 0; s < 8; ++s) neg[s] = (signs && signs[8 * j + s] < 0) ? 0x80000000u : 0u;
+  for (int s = 0; s < 16; ++s) neg[s] = (signs && signs[16 * j + s] < 0) ? 0x80000000u : 0u;
 }
 
 // x from lane i ^ M within the 16-lane DPP row, as VALU moves (no LDS):
 // M = 1, 2 are quad permutations; M = 4 is the quad permutation i ^ 3
-// followed by the half-row mirror (i ^ 7); M = 8 the half-row mirror
-// followed by the row mirror (i ^ 15).
+// followed by the half-row mirror (i ^ 7).
 template <int M>
 __device__ __forceinline__ float lane_xor(float x) {
   const int v = __float_as_int(x);
   constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kQuadXor3 = 0x1B;
-  constexpr int kRowMirror = 0x140, kHalfMirror = 0x141;
+  constexpr int kHalfMirror = 0x141;
   int r;
   if constexpr (M == 1) {
     r = __builtin_amdgcn_mov_dpp(v, kQuadXor1, 0xF, 0xF, true);
   } else if constexpr (M == 2) {
     r = __builtin_amdgcn_mov_dpp(v, kQuadXor2, 0xF, 0xF, true);
-  } else if constexpr (M == 4) {
+  } else {
+    static_assert(M == 4, "lane distance within an 8-lane group");
     r = __builtin_amdgcn_mov_dpp(v, kQuadXor3, 0xF, 0xF, true);
     r = __builtin_amdgcn_mov_dpp(r, kHalfMirror, 0xF, 0xF, true);
-  } else {
-    static_assert(M == 8, "lane distance within a 16-lane row");
-    r = __builtin_amdgcn_mov_dpp(v, kHalfMirror, 0xF, 0xF, true);
-    r = __builtin_amdgcn_mov_dpp(r, kRowMirror, 0xF, 0xF, true);
   }
   return __int_as_float(r);
 }
@@ -89,49 +88,58 @@ __device__ __forceinline__ float lane_xor(float x) {
 // keeps a + b, its partner a - b, i.e. partner's value + (+-1) * own value
 // (one exact FMA: the product by +-1 does not round).
 template <int M>
-__device__ __forceinline__ void lane_butterfly(float (&v)[8], int j) {
+__device__ __forceinline__ void lane_butterfly(float (&v)[16], int j) {
   const float sgn = (j & M) ? -1.0f : 1.0f;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) v[s] = fmaf(sgn, v[s], lane_xor<M>(v[s]));
+  for (int s = 0; s < 16; ++s) v[s] = fmaf(sgn, v[s], lane_xor<M>(v[s]));
 }
 
-// This lane's 16 bytes of row `row` (zeros past the last row).
+// This lane's 32 bytes of row `row` (zeros past the last row).
+struct Row16 {
+  u16x8 lo, hi;
+};
 template <int D>
-__device__ __forceinline__ u16x8 load_row(const uint16_t* x, int row, int rows, int j) {
-  u16x8 w = {};
-  if (row < rows) w = *reinterpret_cast<const u16x8*>(x + (size_t)row * D + 8 * j);
+__device__ __forceinline__ Row16 load_row(const uint16_t* x, int row, int rows, int j) {
+  Row16 w = {};
+  if (row < rows) {
+    const u16x8* src = reinterpret_cast<const u16x8*>(x + (size_t)row * D + 16 * j);
+    w.lo = src[0];
+    w.hi = src[1];
+  }
   return w;
 }
 
-// The lane's 8 values as fp32 and, when `rotate`, with the signs applied
+// The lane's 16 values as fp32 and, when `rotate`, with the signs applied
 // and the Walsh-Hadamard transform of the row.
 template <int D>
-__device__ __forceinline__ void transform(u16x8 w, const unsigned (&neg)[8], bool rotate, int j,
-                                          float (&v)[8]) {
+__device__ __forceinline__ void transform(Row16 w, const unsigned (&neg)[16], bool rotate, int j,
+                                          float (&v)[16]) {
 #pragma unroll
-  for (int s = 0; s < 8; ++s) v[s] = __uint_as_float(((unsigned)w[s] << 16) ^ neg[s]);
+  for (int s = 0; s < 8; ++s) {
+    v[s] = __uint_as_float(((unsigned)w.lo[s] << 16) ^ neg[s]);
+    v[s + 8] = __uint_as_float(((unsigned)w.hi[s] << 16) ^ neg[s + 8]);
+  }
   if (!rotate) return;
-  // Butterflies over index bits 0..2 (inside the lane).
+  // Butterflies over index bits 0..3 (inside the lane).
 #pragma unroll
-  for (int h = 1; h < 8; h <<= 1)
+  for (int h = 1; h < 16; h <<= 1)
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+    for (int s = 0; s < 16; ++s)
       if ((s & h) == 0) {
         const float a = v[s], b = v[s + h];
         v[s] = a + b;
         v[s + h] = a - b;
       }
-  // Butterflies over index bits 3.. (lane bit m of the row).
+  // Butterflies over index bits 4.. (lane bit m of the row).
   lane_butterfly<1>(v, j);
   lane_butterfly<2>(v, j);
-  lane_butterfly<4>(v, j);
-  if constexpr (QShape<D>::L == 16) lane_butterfly<8>(v, j);
+  if constexpr (QShape<D>::L == 8) lane_butterfly<4>(v, j);
 }
 
 // Rows are visited in steps of kQuantUnroll row groups per workgroup, whose
 // loads are all issued before the first transform (more bytes in flight per
 // wave).
-constexpr int kQuantUnroll = 4;
+constexpr int kQuantUnroll = 2;
 
 __device__ __forceinline__ float block_max(float x, float* red) {
 #pragma unroll
@@ -152,20 +160,20 @@ __device__ __forceinline__ void absmax_body(const QuantParams& p) {
   const int lane = threadIdx.x & 63;
   const int j = lane % S::L;
   const int r_in = (threadIdx.x >> 6) * S::RPW + lane / S::L;
-  unsigned neg[8];
+  unsigned neg[16];
   sign_masks(p.signs, j, neg);
   float mx = 0.f;
   const int stride = gridDim.x * S::RPB;
   for (int r0 = blockIdx.x * S::RPB; r0 < p.rows; r0 += kQuantUnroll * stride) {
-    u16x8 w[kQuantUnroll];
+    Row16 w[kQuantUnroll];
 #pragma unroll
     for (int u = 0; u < kQuantUnroll; ++u) w[u] = load_row<D>(p.x, r0 + u * stride + r_in, p.rows, j);
 #pragma unroll
     for (int u = 0; u < kQuantUnroll; ++u) {
-      float v[8];
+      float v[16];
       transform<D>(w[u], neg, p.signs != nullptr, j, v);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) mx = fmaxf(mx, fabsf(v[s]));
+      for (int s = 0; s < 16; ++s) mx = fmaxf(mx, fabsf(v[s]));
     }
   }
   mx = block_max(mx, red);
@@ -186,32 +194,30 @@ __device__ __forceinline__ void quant_body(const QuantParams& p) {
   const int lane = threadIdx.x & 63;
   const int j = lane % S::L;
   const int r_in = (threadIdx.x >> 6) * S::RPW + lane / S::L;
-  unsigned neg[8];
+  unsigned neg[16];
   sign_masks(p.signs, j, neg);
   const int stride = gridDim.x * S::RPB;
   for (int r0 = blockIdx.x * S::RPB; r0 < p.rows; r0 += kQuantUnroll * stride) {
-    u16x8 w[kQuantUnroll];
+    Row16 w[kQuantUnroll];
 #pragma unroll
     for (int u = 0; u < kQuantUnroll; ++u) w[u] = load_row<D>(p.x, r0 + u * stride + r_in, p.rows, j);
 #pragma unroll
     for (int u = 0; u < kQuantUnroll; ++u) {
       const int row = r0 + u * stride + r_in;
-      float v[8];
+      float v[16];
       transform<D>(w[u], neg, p.signs != nullptr, j, v);
-      float c[8];
+      float c[16];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) c[s] = fminf(fmaxf(v[s] * inv, -448.0f), 448.0f);
-      // Byte t of the 8-byte group is element 8j + t.
-      unsigned lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
-      lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
-      unsigned hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
-      hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], hi, true);
-      if (row < p.rows) {
-        uint2 o;
-        o.x = lo;
-        o.y = hi;
-        *reinterpret_cast<uint2*>(p.codes + (size_t)row * D + 8 * j) = o;
+      for (int s = 0; s < 16; ++s) c[s] = fminf(fmaxf(v[s] * inv, -448.0f), 448.0f);
+      // Byte t of the 16-byte group is element 16j + t.
+      unsigned o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        o[q] = __builtin_amdgcn_cvt_pk_fp8_f32(c[4 * q], c[4 * q + 1], 0, false);
+        o[q] = __builtin_amdgcn_cvt_pk_fp8_f32(c[4 * q + 2], c[4 * q + 3], o[q], true);
       }
+      if (row < p.rows)
+        *reinterpret_cast<uint4*>(p.codes + (size_t)row * D + 16 * j) = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
 }
@@ -235,7 +241,7 @@ FA_FP8_QUANT_KERNELS(128)
 namespace fa {
 
 int quant_blocks(int rows, int d) {
-  const int rpb = (64 / (d / 8)) * (kQuantThreads / 64);
+  const int rpb = (64 / (d / 16)) * (kQuantThreads / 64);
   const long long need = ((long long)rows + rpb - 1) / rpb;
   return (int)(need < kQuantMaxBlocks ? need : kQuantMaxBlocks);
 }

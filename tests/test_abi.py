@@ -318,11 +318,13 @@ def test_quantize_names_and_workspace():
     assert fa.fa_fp8_quantize_kernel_name(64, 1) == "fa_fp8_quant_d64"
     assert fa.fa_fp8_quantize_kernel_name(32, 0) is None
     assert fa.fa_fp8_quantize_kernel_name(128, 2) is None
-    # One float per workgroup of the first pass: 16 rows (d = 128) or 32
+    # One float per workgroup of the first pass: 32 rows (d = 128) or 64
     # rows (d = 64) per workgroup, at most 1024 workgroups.
     assert fa.fa_fp8_quantize_workspace_size(1, 128) == 4
-    assert fa.fa_fp8_quantize_workspace_size(17, 128) == 8
-    assert fa.fa_fp8_quantize_workspace_size(33, 64) == 8
+    assert fa.fa_fp8_quantize_workspace_size(32, 128) == 4
+    assert fa.fa_fp8_quantize_workspace_size(33, 128) == 8
+    assert fa.fa_fp8_quantize_workspace_size(64, 64) == 4
+    assert fa.fa_fp8_quantize_workspace_size(65, 64) == 8
     assert fa.fa_fp8_quantize_workspace_size(32 * 16384, 128) == 4096
     assert fa.fa_fp8_quantize_workspace_size(0, 128) == 0
     assert fa.fa_fp8_quantize_workspace_size(16, 256) == 0
