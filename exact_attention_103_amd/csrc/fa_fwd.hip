@@ -127,7 +127,7 @@ __device__ __forceinline__ void load_tile(const uint16_t* base, int j0, int Nk, 
   }
 }
 
-template <int D, int BN, int NW, int NQB, bool CAUSAL, bool SKIP_IDLE>
+template <int D, int BN, int NW, int NQB, bool CAUSAL, bool SKIP_IDLE, bool HEAD_MAJOR>
 __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_char* kb1,
                                          lds_char* vb0, lds_char* vb1) {
   using S = FwdShape<D, BN, NW, NQB>;
@@ -140,12 +140,28 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
   const int hl = lane >> 5;   // lane half: k sub-block of the MFMA operands
   const int n = lane & 31;    // query column of S^T / O^T owned by this lane
 
-  // Grid: query block major (descending when causal, so the longest
-  // workgroups start first), (batch, head) minor.
+  // Grid order.  Workgroups go to the 8 XCDs round-robin (workgroup w to XCD
+  // w mod 8), each with its own L2.  By default the order is query block
+  // major (descending when causal, so the longest workgroups start first)
+  // and (batch, head) minor: each XCD keeps a few heads and runs several
+  // query blocks of each at once, sharing their K/V tiles in its L2.  With
+  // HEAD_MAJOR (and a head count divisible by 8) each XCD instead walks its
+  // heads one after the other, each head's query blocks longest first, so
+  // every workgroup of the XCD streams the same K/V tiles at the same time:
+  // half the HBM reads at the long workload.  It is used for the 256-row
+  // tiles (long key ranges); with few query blocks per head the late start
+  // of a head's longest blocks unbalances the XCD.
   const int BH = p.B * p.Hq;
   const int nqb = (p.Nq + S::BM - 1) / S::BM;
-  const int bh = blockIdx.x % BH;
-  const int qi = blockIdx.x / BH;
+  int bh, qi;
+  if (HEAD_MAJOR && BH % 8 == 0) {
+    const int x = blockIdx.x % 8, i = blockIdx.x / 8;
+    bh = x + 8 * (i / nqb);
+    qi = i % nqb;
+  } else {
+    bh = blockIdx.x % BH;
+    qi = blockIdx.x / BH;
+  }
   const int qblk = CAUSAL ? (nqb - 1 - qi) : qi;
   const int b = bh / p.Hq;
   const int h = bh - b * p.Hq;
@@ -407,7 +423,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
 
 // Kernel symbols carry plain C names so that a profiler trace names exactly
 // which variant ran.
-#define FA_FWD_KERNEL(NAME, D, BN, NW, NQB, CAUSAL, WAVES_PER_EU, SKIP_IDLE)         \
+#define FA_FWD_KERNEL(NAME, D, BN, NW, NQB, CAUSAL, WAVES_PER_EU, SKIP_IDLE, HEAD_MAJOR) \
   extern "C" __global__ void __launch_bounds__(64 * NW, WAVES_PER_EU) NAME(           \
       fa::FwdParams p) {                                                              \
     using Sh = fa::FwdShape<D, BN, NW, NQB>;                                          \
@@ -415,26 +431,26 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
     __shared__ __attribute__((aligned(1024))) char k1[Sh::TILE];                      \
     __shared__ __attribute__((aligned(1024))) char v0[Sh::TILE];                      \
     __shared__ __attribute__((aligned(1024))) char v1[Sh::TILE];                      \
-    fa::fwd_body<D, BN, NW, NQB, CAUSAL, SKIP_IDLE>(p, (fa::lds_char*)k0,              \
+    fa::fwd_body<D, BN, NW, NQB, CAUSAL, SKIP_IDLE, HEAD_MAJOR>(p, (fa::lds_char*)k0,  \
         (fa::lds_char*)k1, (fa::lds_char*)v0, (fa::lds_char*)v1);                     \
   }
 
 // Tile table (head dim: keys per tile, waves, query blocks of 32 rows per
-// wave, waves per SIMD, causal idle-tile skip).  It must match fwd_tile()
+// wave, waves per SIMD, causal idle-tile skip, head-major XCD order).  It must match fwd_tile()
 // below.  d = 128 has a 256-row tile (8 waves share each K/V tile, for long
 // key ranges) and a 128-row tile (more workgroups per CU, for short ones).
 // The idle-tile skip measured +0.4% (d = 128, 16k keys), +2% (d = 128, 2k
 // keys) and +3% (d = 32) but -3% at d = 64 and -0.3% at d = 256.
-FA_FWD_KERNEL(fa_fwd_d32_nomask, 32, 128, 4, 1, false, 2, false)
-FA_FWD_KERNEL(fa_fwd_d32_causal, 32, 128, 4, 1, true, 2, true)
-FA_FWD_KERNEL(fa_fwd_d64_nomask, 64, 64, 4, 1, false, 2, false)
-FA_FWD_KERNEL(fa_fwd_d64_causal, 64, 64, 4, 1, true, 2, false)
-FA_FWD_KERNEL(fa_fwd_d128_nomask, 128, 64, 8, 1, false, 2, false)
-FA_FWD_KERNEL(fa_fwd_d128_causal, 128, 64, 8, 1, true, 2, true)
-FA_FWD_KERNEL(fa_fwd_d128_nomask_bm128, 128, 64, 4, 1, false, 2, false)
-FA_FWD_KERNEL(fa_fwd_d128_causal_bm128, 128, 64, 4, 1, true, 2, true)
-FA_FWD_KERNEL(fa_fwd_d256_nomask, 256, 32, 4, 1, false, 1, false)
-FA_FWD_KERNEL(fa_fwd_d256_causal, 256, 32, 4, 1, true, 1, false)
+FA_FWD_KERNEL(fa_fwd_d32_nomask, 32, 128, 4, 1, false, 2, false, false)
+FA_FWD_KERNEL(fa_fwd_d32_causal, 32, 128, 4, 1, true, 2, true, false)
+FA_FWD_KERNEL(fa_fwd_d64_nomask, 64, 64, 4, 1, false, 2, false, false)
+FA_FWD_KERNEL(fa_fwd_d64_causal, 64, 64, 4, 1, true, 2, false, false)
+FA_FWD_KERNEL(fa_fwd_d128_nomask, 128, 64, 8, 1, false, 2, false, true)
+FA_FWD_KERNEL(fa_fwd_d128_causal, 128, 64, 8, 1, true, 2, true, true)
+FA_FWD_KERNEL(fa_fwd_d128_nomask_bm128, 128, 64, 4, 1, false, 2, false, false)
+FA_FWD_KERNEL(fa_fwd_d128_causal_bm128, 128, 64, 4, 1, true, 2, true, false)
+FA_FWD_KERNEL(fa_fwd_d256_nomask, 256, 32, 4, 1, false, 1, false, false)
+FA_FWD_KERNEL(fa_fwd_d256_causal, 256, 32, 4, 1, true, 1, false, false)
 
 namespace fa {
 namespace {
