@@ -209,11 +209,13 @@ __device__ __forceinline__ void quant_body(const QuantParams& p) {
       float c[16];
 #pragma unroll
       for (int s = 0; s < 16; ++s) c[s] = fminf(fmaxf(v[s] * inv, -448.0f), 448.0f);
-      // Byte t of the 16-byte group is element 16j + t.
+      // Byte t of the 16-byte group is element 16j + t.  The two conversions
+      // of a dword overwrite both halves, so its "old" operand is only a
+      // register to write into: the first source, dead afterwards.
       unsigned o[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        o[q] = __builtin_amdgcn_cvt_pk_fp8_f32(c[4 * q], c[4 * q + 1], 0, false);
+        o[q] = __builtin_amdgcn_cvt_pk_fp8_f32(c[4 * q], c[4 * q + 1], __float_as_int(c[4 * q]), false);
         o[q] = __builtin_amdgcn_cvt_pk_fp8_f32(c[4 * q + 2], c[4 * q + 3], o[q], true);
       }
       if (row < p.rows)

@@ -208,6 +208,7 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
     return f8_half_max(x) * cexp;
   };
 
+  v8i pf = v8i{};   // fp8 P^T of the current tile (B operand of the PV products)
   auto step = [&](const lds_char* kr, const lds_char* vr, lds_char* kw, lds_char* vw,
                   f32x16 (&sc)[S::KB], f32x16 (&sn)[S::KB], int j) {
     const int j0 = j * BN;
@@ -222,8 +223,10 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
 
     // P^T = 2^(S*c - m) rounded to fp8: dword w holds keys of block w/4,
     // registers 4(w%4) .. +3, which the V^T reads below follow.  The second
-    // pass runs only after the reference moved (see kF8SumLimit).
-    v8i pf;
+    // pass runs only after the reference moved (see kF8SumLimit).  The two
+    // conversions of dword w overwrite both of its halves; passing the
+    // previous tile's dword as the "old" operand keeps the same registers
+    // and saves zeroing them every tile.
     float t0, t1;
     for (int pass = 0;; ++pass) {
       const float nm = -m_run;
@@ -238,7 +241,7 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
         const float e3 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 3], cexp, nm));
         t0 += e0 + e2;
         t1 += e1 + e3;
-        int x = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, pf[w], false);
         x = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, x, true);
         pf[w] = x;
       }
