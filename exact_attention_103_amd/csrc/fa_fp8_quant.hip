@@ -48,6 +48,8 @@ constexpr int kQuantThreads = 256;
 constexpr int kQuantMaxBlocks = 1024;
 
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char;
 
 template <int D>
 struct QShape {
@@ -109,20 +111,22 @@ __device__ __forceinline__ Row16 load_row(const uint16_t* x, int row, int rows, 
   return w;
 }
 
-// The lane's 16 values as fp32 and, when `rotate`, with the signs applied
-// and the Walsh-Hadamard transform of the row.
-template <int D>
-__device__ __forceinline__ void transform(Row16 w, const unsigned (&neg)[16], bool rotate, int j,
-                                          float (&v)[16]) {
+// The lane's 16 bf16 values as fp32, with the signs applied.
+__device__ __forceinline__ void to_f32(Row16 w, const unsigned (&neg)[16], float (&v)[16]) {
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     v[s] = __uint_as_float(((unsigned)w.lo[s] << 16) ^ neg[s]);
     v[s + 8] = __uint_as_float(((unsigned)w.hi[s] << 16) ^ neg[s + 8]);
   }
-  if (!rotate) return;
-  // Butterflies over index bits 0..3 (inside the lane).
+}
+
+// Butterflies over the bits of `bits` (a set of register index bits):
+// register s with the bit clear keeps a + b, its partner s + h gets a - b.
+template <int BITS>
+__device__ __forceinline__ void inlane_butterflies(float (&v)[16]) {
 #pragma unroll
-  for (int h = 1; h < 16; h <<= 1)
+  for (int h = 1; h < 16; h <<= 1) {
+    if ((BITS & h) == 0) continue;
 #pragma unroll
     for (int s = 0; s < 16; ++s)
       if ((s & h) == 0) {
@@ -130,10 +134,80 @@ __device__ __forceinline__ void transform(Row16 w, const unsigned (&neg)[16], bo
         v[s] = a + b;
         v[s + h] = a - b;
       }
-  // Butterflies over index bits 4.. (lane bit m of the row).
+  }
+}
+
+// The lane's 16 values as fp32 and, when `rotate`, with the signs applied
+// and the Walsh-Hadamard transform of the row (d = 64: index bits 0..3 in
+// the lane, bits 4..5 between lanes through DPP moves).
+template <int D>
+__device__ __forceinline__ void transform(Row16 w, const unsigned (&neg)[16], bool rotate, int j,
+                                          float (&v)[16]) {
+  to_f32(w, neg, v);
+  if (!rotate) return;
+  inlane_butterflies<15>(v);
   lane_butterfly<1>(v, j);
   lane_butterfly<2>(v, j);
   if constexpr (QShape<D>::L == 8) lane_butterfly<4>(v, j);
+}
+
+// d = 128 with rotation: the transform runs entirely inside lanes, with one
+// transpose through LDS per pass.  In row-major order lane j of a row holds
+// elements 16j + c (c = 0..15, index bits 0..3); in column order it holds
+// elements 16k + c for its two columns c = 2j, 2j + 1 and k = 0..7 (index
+// bits 4..6), in registers 2k + (c & 1).  Each wave has its own region per
+// row group: 8 rows of 576 bytes (512 used).  The 16-byte chunk q of group k
+// (elements 16k + 4q .. +3) of row rw sits at chunk q ^ ((k >> 2) | 2 (rw &
+// 1)) of the group's 64 bytes, so that the row-major 16-byte accesses (16
+// lanes per LDS pass: two rows) and the column 8-byte accesses (32 lanes
+// per pass: four rows) each touch all 64 banks once.
+constexpr int kTRowBytes = 576;
+constexpr int kTRegion = 8 * kTRowBytes;
+
+__device__ __forceinline__ int tchunk(int rw, int k, int q) {
+  return rw * kTRowBytes + k * 64 + ((q ^ ((k >> 2) | ((rw & 1) << 1))) << 4);
+}
+
+// Row-major registers (v[c], lane j) -> LDS -> column registers (t[2k + c&1]).
+__device__ __forceinline__ void rows_to_columns(lds_char* reg, int rw, int j, const float (&v)[16],
+                                                float (&t)[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *(__attribute__((address_space(3))) f32x4*)(reg + tchunk(rw, j, q)) =
+        f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const f32x2 x =
+        *(const __attribute__((address_space(3))) f32x2*)(reg + tchunk(rw, k, j >> 1) + 8 * (j & 1));
+    t[2 * k] = x[0];
+    t[2 * k + 1] = x[1];
+  }
+}
+
+// Column registers -> LDS -> row-major registers.
+__device__ __forceinline__ void columns_to_rows(lds_char* reg, int rw, int j, const float (&t)[16],
+                                                float (&v)[16]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    *(__attribute__((address_space(3))) f32x2*)(reg + tchunk(rw, k, j >> 1) + 8 * (j & 1)) =
+        f32x2{t[2 * k], t[2 * k + 1]};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 x = *(const __attribute__((address_space(3))) f32x4*)(reg + tchunk(rw, j, q));
+    v[4 * q] = x[0];
+    v[4 * q + 1] = x[1];
+    v[4 * q + 2] = x[2];
+    v[4 * q + 3] = x[3];
+  }
+}
+
+// Sign-bit masks of the lane's elements in column order (d = 128).
+__device__ __forceinline__ void sign_masks_cols(const int8_t* signs, int j, unsigned (&neg)[16]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      neg[2 * k + h] = (signs && signs[16 * k + 2 * j + h] < 0) ? 0x80000000u : 0u;
 }
 
 // Rows are visited in steps of kQuantUnroll row groups per workgroup, whose
@@ -164,6 +238,32 @@ __device__ __forceinline__ void absmax_body(const QuantParams& p) {
   sign_masks(p.signs, j, neg);
   float mx = 0.f;
   const int stride = gridDim.x * S::RPB;
+  if constexpr (D == 128) {
+    if (p.signs) {
+      // Row-major loads, bits 0..3 in the lane, transpose, bits 4..6 in the lane.
+      __shared__ __attribute__((aligned(16))) char tb[kQuantThreads / 64][kQuantUnroll][kTRegion];
+      const int wave = threadIdx.x >> 6, rw = lane / S::L;
+      for (int r0 = blockIdx.x * S::RPB; r0 < p.rows; r0 += kQuantUnroll * stride) {
+        Row16 w[kQuantUnroll];
+#pragma unroll
+        for (int u = 0; u < kQuantUnroll; ++u)
+          w[u] = load_row<D>(p.x, r0 + u * stride + r_in, p.rows, j);
+#pragma unroll
+        for (int u = 0; u < kQuantUnroll; ++u) {
+          float v[16], t[16];
+          to_f32(w[u], neg, v);
+          inlane_butterflies<15>(v);
+          rows_to_columns((lds_char*)tb[wave][u], rw, j, v, t);
+          inlane_butterflies<14>(t);
+#pragma unroll
+          for (int s = 0; s < 16; ++s) mx = fmaxf(mx, fabsf(t[s]));
+        }
+      }
+      mx = block_max(mx, red);
+      if (threadIdx.x == 0) p.partial[blockIdx.x] = mx;
+      return;
+    }
+  }
   for (int r0 = blockIdx.x * S::RPB; r0 < p.rows; r0 += kQuantUnroll * stride) {
     Row16 w[kQuantUnroll];
 #pragma unroll
@@ -194,32 +294,71 @@ __device__ __forceinline__ void quant_body(const QuantParams& p) {
   const int lane = threadIdx.x & 63;
   const int j = lane % S::L;
   const int r_in = (threadIdx.x >> 6) * S::RPW + lane / S::L;
+  const int stride = gridDim.x * S::RPB;
+  // Codes of one row group: byte t of the lane's 16-byte group is element
+  // 16j + t.  The two conversions of a dword overwrite both halves, so its
+  // "old" operand is only a register to write into: the first source, dead
+  // afterwards.
+  auto store_codes = [&](int row, const float (&v)[16]) {
+    float c[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) c[s] = fminf(fmaxf(v[s] * inv, -448.0f), 448.0f);
+    unsigned o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o[q] = __builtin_amdgcn_cvt_pk_fp8_f32(c[4 * q], c[4 * q + 1], __float_as_int(c[4 * q]), false);
+      o[q] = __builtin_amdgcn_cvt_pk_fp8_f32(c[4 * q + 2], c[4 * q + 3], o[q], true);
+    }
+    if (row < p.rows)
+      *reinterpret_cast<uint4*>(p.codes + (size_t)row * D + 16 * j) = make_uint4(o[0], o[1], o[2], o[3]);
+  };
+  if constexpr (D == 128) {
+    if (p.signs) {
+      // Column-order loads (4 bytes: elements 16k + 2j, 16k + 2j + 1), bits
+      // 4..6 in the lane, transpose, bits 0..3 in the lane, row-major store.
+      __shared__ __attribute__((aligned(16))) char tb[kQuantThreads / 64][kQuantUnroll][kTRegion];
+      const int wave = threadIdx.x >> 6, rw = lane / S::L;
+      unsigned negc[16];
+      sign_masks_cols(p.signs, j, negc);
+      for (int r0 = blockIdx.x * S::RPB; r0 < p.rows; r0 += kQuantUnroll * stride) {
+        unsigned w[kQuantUnroll][8];
+#pragma unroll
+        for (int u = 0; u < kQuantUnroll; ++u) {
+          const int row = r0 + u * stride + r_in;
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            w[u][k] = row < p.rows
+                          ? *reinterpret_cast<const unsigned*>(p.x + (size_t)row * D + 16 * k + 2 * j)
+                          : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kQuantUnroll; ++u) {
+          float t[16], v[16];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            t[2 * k] = __uint_as_float((w[u][k] << 16) ^ negc[2 * k]);
+            t[2 * k + 1] = __uint_as_float((w[u][k] & 0xFFFF0000u) ^ negc[2 * k + 1]);
+          }
+          inlane_butterflies<14>(t);
+          columns_to_rows((lds_char*)tb[wave][u], rw, j, t, v);
+          inlane_butterflies<15>(v);
+          store_codes(r0 + u * stride + r_in, v);
+        }
+      }
+      return;
+    }
+  }
   unsigned neg[16];
   sign_masks(p.signs, j, neg);
-  const int stride = gridDim.x * S::RPB;
   for (int r0 = blockIdx.x * S::RPB; r0 < p.rows; r0 += kQuantUnroll * stride) {
     Row16 w[kQuantUnroll];
 #pragma unroll
     for (int u = 0; u < kQuantUnroll; ++u) w[u] = load_row<D>(p.x, r0 + u * stride + r_in, p.rows, j);
 #pragma unroll
     for (int u = 0; u < kQuantUnroll; ++u) {
-      const int row = r0 + u * stride + r_in;
       float v[16];
       transform<D>(w[u], neg, p.signs != nullptr, j, v);
-      float c[16];
-#pragma unroll
-      for (int s = 0; s < 16; ++s) c[s] = fminf(fmaxf(v[s] * inv, -448.0f), 448.0f);
-      // Byte t of the 16-byte group is element 16j + t.  The two conversions
-      // of a dword overwrite both halves, so its "old" operand is only a
-      // register to write into: the first source, dead afterwards.
-      unsigned o[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        o[q] = __builtin_amdgcn_cvt_pk_fp8_f32(c[4 * q], c[4 * q + 1], __float_as_int(c[4 * q]), false);
-        o[q] = __builtin_amdgcn_cvt_pk_fp8_f32(c[4 * q + 2], c[4 * q + 3], o[q], true);
-      }
-      if (row < p.rows)
-        *reinterpret_cast<uint4*>(p.codes + (size_t)row * D + 16 * j) = make_uint4(o[0], o[1], o[2], o[3]);
+      store_codes(r0 + u * stride + r_in, v);
     }
   }
 }
