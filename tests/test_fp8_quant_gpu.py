@@ -64,6 +64,9 @@ CASES = [  # (rows, d, rotated, outliers)
     (1, 128, True, False), (7, 64, True, False), (33, 128, True, True), (1000, 64, False, False),
     (1000, 128, False, True), (20000, 128, True, False), (4097, 64, True, True),
     (300, 128, True, True),
+    # 8 rows: one wave's row group, the other waves idle; 50001 rows: the
+    # grid's second row group per iteration ends partway.
+    (8, 128, True, True), (50001, 128, True, False),
 ]
 
 
