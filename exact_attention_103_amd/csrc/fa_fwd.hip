@@ -149,12 +149,15 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
   // heads one after the other, each head's query blocks longest first, so
   // every workgroup of the XCD streams the same K/V tiles at the same time:
   // half the HBM reads at the long workload.  It is used for the 256-row
-  // tiles (long key ranges); with few query blocks per head the late start
-  // of a head's longest blocks unbalances the XCD.
+  // tiles (long key ranges).  When causal, the XCD's last head then starts
+  // its longest block (about nqb key tiles) late; that block still ends in
+  // time only if it is no longer than one head's share of the XCD (about
+  // nqb^2/64 tiles per CU), i.e. for nqb >= 64.  With fewer query blocks per
+  // head the order stays block major (16 blocks per head measured -25%).
   const int BH = p.B * p.Hq;
   const int nqb = (p.Nq + S::BM - 1) / S::BM;
   int bh, qi;
-  if (HEAD_MAJOR && BH % 8 == 0) {
+  if (HEAD_MAJOR && BH % 8 == 0 && (!CAUSAL || nqb >= 64)) {
     const int x = blockIdx.x % 8, i = blockIdx.x / 8;
     bh = x + 8 * (i / nqb);
     qi = i % nqb;
