@@ -439,9 +439,10 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
   }
 
 // Tile table (head dim: keys per tile, waves, query blocks of 32 rows per
-// wave, waves per SIMD, causal idle-tile skip, head-major XCD order).  It must match fwd_tile()
-// below.  d = 128 has a 256-row tile (8 waves share each K/V tile, for long
-// key ranges) and a 128-row tile (more workgroups per CU, for short ones).
+// wave, waves per SIMD, causal idle-tile skip, head-major XCD order).  It
+// must match fwd_tile() below.  d = 128 has a 256-row tile (8 waves share
+// each K/V tile, for long key ranges) and a 128-row tile (more workgroups
+// per CU, for short ones).
 // The idle-tile skip measured +0.4% (d = 128, 16k keys), +2% (d = 128, 2k
 // keys) and +3% (d = 32) but -3% at d = 64 and -0.3% at d = 256.
 FA_FWD_KERNEL(fa_fwd_d32_nomask, 32, 128, 4, 1, false, 2, false, false)
