@@ -70,6 +70,7 @@ FWD = [  # (B, Hq, Hkv, Nq, Nk, d, causal)
     (1, 4, 2, 1000, 1000, 128, True),     # 128-row tile
     (1, 2, 1, 4500, 4500, 128, True),     # 256-row tile (long key range)
     (1, 2, 2, 700, 2100, 128, False),     # 256-row tile, non-causal
+    (1, 8, 2, 300, 2100, 128, False),     # 256-row tile, head-major XCD order
     (1, 4, 4, 1000, 1000, 256, True),
     (1, 2, 1, 65, 1000, 256, False),
 ]
