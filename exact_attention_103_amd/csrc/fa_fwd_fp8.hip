@@ -108,10 +108,24 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
   const int hl = lane >> 5;
   const int n = lane & 31;
 
+  // Grid order as in the bf16 forward: query block major (longest causal
+  // blocks first), (batch, head) minor; non-causal grids with a head count
+  // divisible by 8 run head major inside each XCD (workgroup w goes to XCD
+  // w mod 8), so the XCD's workgroups stream the same K/V tiles together.
+  // Measured: +2.4% at B=8 H=16 N=2048 non-causal; at the long causal
+  // workload head-major order was 2.9% slower here, so causal grids keep
+  // the block-major order.
   const int BH = p.B * p.Hq;
   const int nqb = (p.Nq + S::BM - 1) / S::BM;
-  const int bh = blockIdx.x % BH;
-  const int qi = blockIdx.x / BH;
+  int bh, qi;
+  if (!CAUSAL && BH % 8 == 0) {
+    const int x = blockIdx.x % 8, i = blockIdx.x / 8;
+    bh = x + 8 * (i / nqb);
+    qi = i % nqb;
+  } else {
+    bh = blockIdx.x % BH;
+    qi = blockIdx.x / BH;
+  }
   const int qblk = CAUSAL ? (nqb - 1 - qi) : qi;
   const int b = bh / p.Hq;
   const int h = bh - b * p.Hq;
