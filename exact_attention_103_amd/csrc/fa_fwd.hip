@@ -315,11 +315,12 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
     // products keeps a single S^T tile live.
     if constexpr (kPipe) s_tile(kr, sn);
 
-    // With 8 waves per workgroup (the 256-row tiles), LLVM's instruction
-    // group strategy 0 (LDS reads interleaved with the MFMAs) schedules this
-    // section: +2.6% at the long causal prefill and +2.8% at the causal
-    // B=2 H=16 N=4096 shape; the 128-row tile measured -1% with it.
-    if constexpr (NW == 8) __builtin_amdgcn_iglp_opt(0);
+    // With 8 waves per workgroup (the 256-row tiles) and at d = 256, LLVM's
+    // instruction group strategy 0 (LDS reads interleaved with the MFMAs)
+    // schedules this section: +2.6% at the long causal prefill, +2.8% at the
+    // causal B=2 H=16 N=4096 shape, +5.6% at d = 256 on that shape.  The
+    // 128-row d = 128 tile measured -1% with it and d = 64 -3.8%.
+    if constexpr (NW == 8 || D == 256) __builtin_amdgcn_iglp_opt(0);
     // Per 16-key chunk kc: probabilities P = 2^(S*c - m) become the bf16 B
     // operand (registers 8*(kc%2).. of block kc/2), then O^T += V^T P^T for
     // every d block, the V^T operand coming from two transposing reads and
