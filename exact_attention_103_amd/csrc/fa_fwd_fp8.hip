@@ -235,10 +235,11 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
     // S^T of tile j+1 on the MFMA pipe next to tile j's softmax.
     s_tile(kr, sn);
 
-    // LLVM's instruction group strategy 0 (LDS reads interleaved with the
-    // MFMAs) schedules this section: +2.3% at the long causal prefill, +2.6%
-    // at B=8 H=16 N=2048 non-causal.
-    __builtin_amdgcn_iglp_opt(0);
+    // At d = 128, LLVM's instruction group strategy 0 (LDS reads interleaved
+    // with the MFMAs) schedules this section: +2.3% at the long causal
+    // prefill, +2.6% at B=8 H=16 N=2048 non-causal, +5.3% at B=2 H=16 N=4096
+    // causal.  At d = 64 it measured about -4%.
+    if constexpr (D == 128) __builtin_amdgcn_iglp_opt(0);
     // P^T = 2^(S*c - m) rounded to fp8: dword w holds keys of block w/4,
     // registers 4(w%4) .. +3, which the V^T reads below follow.  The second
     // pass runs only after the reference moved (see kF8SumLimit).  The two
