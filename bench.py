@@ -5,8 +5,9 @@ One step = one causal prefill forward over the long-context workload
 workload (B=8, Hq=32, Hkv=8, Nk=32768, d=128), both through the C ABI on the
 same stream, inputs already resident in HBM.  Prints one JSON line:
 
-  value     prefill TFLOP/s, flop = 4*B*H*N*N*d / 2 (causal), per forward
-            launch (HIP events on the launch stream, averaged over the steps)
+  value     prefill TFLOP/s, flop = 4*B*H*N*N*d / 2 (causal), over the median
+            forward launch duration (HIP events on the launch stream around
+            each launch); the mean is reported next to it
   decode    split-KV decode GB/s, bytes = K + V cache read once + q + O + LSE
   roofline  the forward kernel against the dense bf16 MFMA peak (2.5 PFLOP/s);
             decode carries its own roofline against 8 TB/s HBM
@@ -20,9 +21,20 @@ same stream, inputs already resident in HBM.  Prints one JSON line:
             over its own launches; TFLOP/s counts the algorithmic 5 products
             of the backward (10*B*H*N*N*d / 2 flop, causal), not the 7 the
             recomputation performs
+  workloads after the timed steps: the forward on the training shape
+            (B=8 H=16 N=2048 d=128, causal and not) and on the head-dim sweep
+            (B=2 H=16 N=4096 causal, d = 32, 64, 128, 256), each with its
+            kernel name, median TFLOP/s and roofline: the MFMA peak for
+            d >= 128, the VALU softmax bound (see alu_peak_tflops) for d <= 64
+  sclk      shader clock samples (amd-smi) taken during a sustained run of
+            the prefill after the timed steps
+
+Every timed series is preceded by a warm-up of at least 200 ms of the same
+launches (and at least --warmup steps): the clock ramps up over the first
+tens of milliseconds of sustained work.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bwd]
-                      [--no-fp8]
+                      [--no-fp8] [--no-workloads] [--no-sclk]
 """
 
 from __future__ import annotations
@@ -45,6 +57,74 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 METRIC = "fused attn fwd TFLOP/s (% bf16 MFMA peak); split-KV decode HBM GB/s"
+WARM_MS = 200.0             # minimum warm-up of every timed series
+
+# VALU bound of the softmax (head dims whose MFMA work is too small to hide
+# it).  Per (query, key) pair the online softmax needs at least one exponential
+# and three other wave64 VALU instructions per 64 pairs: the FMA that applies
+# scale*log2(e) and subtracts the running maximum, the add into the row sum,
+# half a v_max3 for the row maximum and half a v_cvt_pk_bf16_f32 for the bf16
+# probabilities.  A wave64 fp32 VALU instruction occupies a 16-lane SIMD for 4
+# cycles; v_exp_f32 was measured on MI355X to issue every 9.5 cycles (8 waves
+# per SIMD, independent chains).  So one SIMD turns at most 64 pairs into
+# probabilities every 9.5 + 3*4 = 21.5 cycles; 1024 SIMDs at 2.4 GHz give
+# 7.3e12 pairs/s, i.e. 4d flop per pair -> 935 TFLOP/s at d = 32, 1871 at
+# d = 64 (and 3741 at d = 128, above the MFMA peak, which then binds).
+EXP_ISSUE_CYCLES = 9.5
+VALU_ISSUE_CYCLES = 4.0
+MIN_VALU_PER_64_PAIRS = 3.0
+SIMDS = 1024
+CLOCK_HZ = 2.4e9
+
+
+def alu_peak_tflops(d):
+    pairs_per_s = SIMDS * CLOCK_HZ * 64 / (EXP_ISSUE_CYCLES + MIN_VALU_PER_64_PAIRS * VALU_ISSUE_CYCLES)
+    return 4 * d * pairs_per_s / 1e12
+
+
+def roofline_for(d, tflops):
+    """The binding roofline of a bf16 forward at head dim d."""
+    alu = alu_peak_tflops(d)
+    if alu < PEAK_BF16_TFLOPS:
+        return {"bound": "alu", "achieved": round(tflops, 2), "peak": round(alu, 1),
+                "unit": "TFLOP/s", "frac": round(tflops / alu, 4),
+                "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
+    return {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
+
+
+def warm(calls, steps):
+    """Run the launch sequence `calls` at least `steps` times and for at least
+    WARM_MS of wall time, then synchronise."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while i < steps or (time.perf_counter() - t0) * 1e3 < WARM_MS:
+        calls()
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return i
+
+
+def time_launches(call, stream, steps, warmup=10):
+    """Per-launch durations (ms) of `call`, from HIP events recorded on the
+    launch stream around each launch, after a time-based warm-up."""
+    import torch
+    warm(call, warmup)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in evs:
+        e[0].record(stream)
+        call()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    return [e[0].elapsed_time(e[1]) for e in evs]
+
+
+def stats(ms):
+    return {"ms": round(float(np.median(ms)), 5), "ms_mean": round(float(np.mean(ms)), 5),
+            "ms_min": round(float(np.min(ms)), 5)}
 
 
 def _dev(bits):
@@ -150,22 +230,13 @@ def fp8_leg(fa, cfg, stream, steps, warmup=20):
         if rc:
             raise fa.FAError(rc, "fa_fwd_fp8")
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    for e in evs:
-        e[0].record(stream)
-        call()
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    ms = [e[0].elapsed_time(e[1]) for e in evs]
-    f_ms = float(np.mean(ms))
+    ms = time_launches(call, stream, steps, warmup)
+    f_ms = float(np.median(ms))
     tf = cfg.flops() / (f_ms * 1e-3) / 1e12
     srcs = ["exact_attention_103_amd/csrc/fa_fwd_fp8.hip", "exact_attention_103_amd/csrc/fa_internal.h"]
     kname = fa.fa_fwd_fp8_kernel_name(cfg.d, int(cfg.causal))
-    return {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(f_ms, 4),
-            "ms_min": round(min(ms), 4), "dtype": "fp8 e4m3 (per-tensor scales), fp32 accumulate",
+    return {"value": round(tf, 2), "unit": "TFLOP/s", **stats(ms),
+            "dtype": "fp8 e4m3 (per-tensor scales), fp32 accumulate",
             "kernel": kname,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
@@ -191,14 +262,11 @@ def quantize_leg(fa, cfg, stream, steps, warmup=20):
     def call(i):
         rc = fa.fa_fp8_quantize(xs[i].data_ptr(), codes[i].data_ptr(), ds[i:].data_ptr(),
                                 signs.data_ptr() if i < 2 else None, rows[i], cfg.d,
-                                wss[i].data_ptr(), wss[i].numel(), sp)
+                                wss[i].data_ptr(), wss[i].numel() * wss[i].element_size(), sp)
         if rc:
             raise fa.FAError(rc, "fa_fp8_quantize")
 
-    for _ in range(warmup):
-        for i in range(3):
-            call(i)
-    torch.cuda.synchronize()
+    warm(lambda: [call(i) for i in range(3)], warmup)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for e in evs:
         e[0].record(stream)
@@ -207,7 +275,7 @@ def quantize_leg(fa, cfg, stream, steps, warmup=20):
         call(1)
         call(2)
     torch.cuda.synchronize()
-    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
     nbytes = 3 * xs[0].numel()
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"tensor": f"Q [{cfg.B}][{cfg.Hq}][{cfg.Nq}][{cfg.d}] bf16, rotated",
@@ -238,25 +306,15 @@ def bwd_leg(fa, cfg, q, k, v, o, lse, stream, steps, warmup=10):
         rc = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cfg.B,
                        cfg.Hq, cfg.Hkv, cfg.Nq, cfg.Nk, cfg.d, cfg.scale, int(cfg.causal),
-                       ws.data_ptr(), ws.numel(), sp)
+                       ws.data_ptr(), ws.numel() * ws.element_size(), sp)
         if rc:
             raise fa.FAError(rc, "fa_bwd")
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    for e in evs:
-        e[0].record(stream)
-        call()
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    ms = [e[0].elapsed_time(e[1]) for e in evs]
-    b_ms = float(np.mean(ms))
+    ms = time_launches(call, stream, steps, warmup)
+    b_ms = float(np.median(ms))
     flop = 2.5 * cfg.flops()
     tf = flop / (b_ms * 1e-3) / 1e12
-    return {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(b_ms, 4),
-            "ms_min": round(min(ms), 4), "flop": flop,
+    return {"value": round(tf, 2), "unit": "TFLOP/s", **stats(ms), "flop": flop,
             "kernels": [fa.fa_bwd_kernel_name(cfg.d, int(cfg.causal), 0),
                         fa.fa_bwd_kernel_name(cfg.d, int(cfg.causal), 1)],
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
@@ -273,6 +331,80 @@ def _bwd_traffic(cfg):
     return None if any(x is None for x in parts) else sum(parts)
 
 
+def workload_legs(fa, stream, steps, names=("train_nc", "train_c", "sweep_d32", "sweep_d64",
+                                             "sweep_d128", "sweep_d256")):
+    """The forward on the training shape and the head-dim sweep, one timed
+    series each (median of per-launch HIP-event durations)."""
+    import torch
+    out = []
+    sp = stream.cuda_stream
+    for name in names:
+        cfg = datagen.CONFIGS[name]
+        q, k, v = (_dev(x) for x in datagen.make_fwd_inputs(cfg))
+        o = torch.empty_like(q)
+        lse = torch.empty((cfg.B, cfg.Hq, cfg.Nq), dtype=torch.float32, device="cuda")
+
+        def call():
+            rc = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           cfg.B, cfg.Hq, cfg.Hkv, cfg.Nq, cfg.Nk, cfg.d, cfg.scale,
+                           int(cfg.causal), sp)
+            if rc:
+                raise fa.FAError(rc, "fa_fwd")
+
+        ms = time_launches(call, stream, steps)
+        st = stats(ms)
+        tf = cfg.flops() / (st["ms"] * 1e-3) / 1e12
+        out.append({"workload": name, "B": cfg.B, "H": cfg.Hq, "N": cfg.Nq, "d": cfg.d,
+                    "causal": cfg.causal, "input_scale": cfg.input_scale,
+                    "kernel": fa.fa_fwd_kernel_name(cfg.d, int(cfg.causal), cfg.Nq, cfg.Nk),
+                    "flop": cfg.flops(), **st, "value": round(tf, 2), "unit": "TFLOP/s",
+                    "roofline": roofline_for(cfg.d, tf)})
+        del q, k, v, o, lse
+    return out
+
+
+def sample_sclk(call, seconds=1.0):
+    """Shader clock (MHz) samples from amd-smi while `call` runs back to back
+    for about `seconds`.  Returns the samples' median/min/max, or a note with
+    the start of amd-smi's reply when no clock could be read from it."""
+    import re
+    import subprocess
+    import threading
+    import torch
+    samples, raw, stop = [], [], threading.Event()
+    cmd = ["amd-smi", "metric", "-g", "0", "-c", "--json"]
+
+    def poll():
+        while not stop.is_set():
+            try:
+                r = subprocess.run(cmd, capture_output=True, text=True, timeout=5)
+            except Exception as e:  # amd-smi missing or hung
+                raw.append(repr(e))
+                return
+            text = r.stdout
+            # the graphics clock block ("gfx_0" / "GFX_0"): first "clk" value in it
+            m = re.search(r'"gfx_0"\s*:\s*\{.*?"clk"\s*:\s*\{\s*"value"\s*:\s*(\d+)', text,
+                          re.S | re.I)
+            if m:
+                samples.append(int(m.group(1)))
+            elif not raw:
+                raw.append((text or r.stderr)[:300])
+
+    th = threading.Thread(target=poll, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            call()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=10)
+    if not samples:
+        return {"mhz_median": None, "note": "no clock parsed", "reply": raw[:1]}
+    return {"mhz_median": float(np.median(samples)), "mhz_min": min(samples),
+            "mhz_max": max(samples), "samples": len(samples), "source": " ".join(cmd)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -282,6 +414,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 forward leg")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the training-shape and head-dim-sweep forward legs")
+    ap.add_argument("--no-sclk", action="store_true", help="skip the shader clock samples")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="instead of the benchmark, run three plain device-to-device "
                          "copies of BYTES bytes (reference dispatches for HBM counters)")
@@ -335,15 +470,14 @@ def main():
             ev[1].record(stream)
         rc = fa.fa_decode_splitkv(qd.data_ptr(), kc.data_ptr(), vc.data_ptr(), od.data_ptr(),
                                   lsed.data_ptr(), dcfg.B, dcfg.Hq, dcfg.Hkv, dcfg.Nk, dcfg.d,
-                                  dcfg.scale, S, ws.data_ptr(), ws.numel(), sp)
+                                  dcfg.scale, S, ws.data_ptr(), ws.numel() * ws.element_size(),
+                                  sp)
         if rc:
             raise fa.FAError(rc, "fa_decode_splitkv")
         if ev is not None:
             ev[2].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_steps = warm(step, args.warmup)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -353,8 +487,8 @@ def main():
     wall = time.perf_counter() - t0
     fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
     dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    f_ms = float(np.mean(fwd_ms))
-    d_ms = float(np.mean(dec_ms))
+    f_ms = float(np.median(fwd_ms))
+    d_ms = float(np.median(dec_ms))
 
     flop = fcfg.flops()
     tflops = flop / (f_ms * 1e-3) / 1e12
@@ -383,13 +517,15 @@ def main():
                         "Hkv=8 Nk=32768 d=128",
             "fwd": {"B": fcfg.B, "H": fcfg.Hq, "N": fcfg.Nq, "d": fcfg.d, "causal": True,
                     "scale": fcfg.scale, "kernel": fa.fa_fwd_kernel_name(fcfg.d, 1, fcfg.Nq, fcfg.Nk),
-                    "flop": flop, "ms": round(f_ms, 5), "ms_min": round(min(fwd_ms), 5)},
+                    "flop": flop, **stats(fwd_ms)},
             "decode": {"B": dcfg.B, "Hq": dcfg.Hq, "Hkv": dcfg.Hkv, "Nk": dcfg.Nk, "d": dcfg.d,
                        "splits": S,
                        "kernels": [fa.fa_decode_kernel_name(dcfg.d, dcfg.Hq // dcfg.Hkv, 0),
                                    fa.fa_decode_kernel_name(dcfg.d, dcfg.Hq // dcfg.Hkv, 1)],
-                       "bytes": dec_bytes, "ms": round(d_ms, 5), "ms_min": round(min(dec_ms), 5)},
+                       "bytes": dec_bytes, **stats(dec_ms)},
             "parallelism": "1 GPU",
+            "warmup_steps_run": warm_steps,
+            "timing": "median of per-launch HIP-event durations on the launch stream",
         },
         "fwd_pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {
@@ -407,6 +543,14 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not args.no_sclk:
+        def fwd_only():
+            fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      fcfg.B, fcfg.Hq, fcfg.Hkv, fcfg.Nq, fcfg.Nk, fcfg.d, fcfg.scale,
+                      int(fcfg.causal), sp)
+        out["sclk"] = sample_sclk(fwd_only)
+    if not args.no_workloads:
+        out["workloads"] = workload_legs(fa, stream, args.steps)
     if not args.no_fp8:
         out["fp8"] = fp8_leg(fa, fcfg, stream, args.steps)
     if not args.no_bwd:

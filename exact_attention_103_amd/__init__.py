@@ -22,7 +22,7 @@ __all__ = [
     "fa_decode_serve", "fa_decode_serve_workspace_size", "fa_decode_serve_num_splits",
     "fa_decode_serve_kernel_name", "fa_fwd_fp8", "fa_fwd_fp8_kernel_name",
     "fa_fwd_fp8_devscale", "fa_fp8_quantize", "fa_fp8_quantize_workspace_size",
-    "fa_fp8_quantize_kernel_name",
+    "fa_fp8_quantize_kernel_name", "fa_build_is_serial",
     "fwd", "fwd_fp8", "fp8_quantize", "decode", "decode_serve", "bwd", "EXPORTED_SYMBOLS",
     "LIB_PATH", "SERIAL_LIB_PATH", "load_library",
 ]
@@ -69,6 +69,7 @@ _SIGNATURES = {
     "fa_fp8_quantize_workspace_size": (_sz, [_i, _i]),
     "fa_fp8_quantize": (_i, [_vp, _vp, _vp, _vp, _i, _i, _vp, _sz, _vp]),
     "fa_fp8_quantize_kernel_name": (_cs, [_i, _i]),
+    "fa_build_is_serial": (_i, []),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -189,6 +190,10 @@ def fa_bwd_kernel_name(d, causal, stage):
     return r.decode() if r else None
 
 
+def fa_build_is_serial():
+    return lib().fa_build_is_serial()
+
+
 def fa_decode_workspace_size(B, Hq, d, num_splits):
     return lib().fa_decode_workspace_size(B, Hq, d, num_splits)
 
@@ -233,6 +238,30 @@ def _check_bf16(name, t, ndim):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _check_out(name, t, dtype, shape, like):
+    """A caller-supplied output must match exactly what the kernel writes:
+    the C ABI sees only a pointer, so an undersized tensor would be
+    overwritten past its end."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_cuda or t.device != like.device:
+        raise ValueError(f"{name} must be on {like.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(t, need, like):
+    """(pointer, size in bytes) of a workspace tensor, allocated when None."""
+    import torch
+    if t is None:
+        t = torch.empty(max(need, 16), dtype=torch.uint8, device=like.device)
+    if not t.is_cuda or t.device != like.device or not t.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {like.device}")
+    return t, t.numel() * t.element_size()
+
+
 def _stream_ptr():
     import torch
     return torch.cuda.current_stream().cuda_stream
@@ -254,6 +283,8 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check_out("out", out, torch.bfloat16, (B, Hq, Nq, d), q)
+    _check_out("lse", lse, torch.float32, (B, Hq, Nq), q)
     rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                 B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), _stream_ptr())
     if rc != FA_OK:
@@ -283,12 +314,12 @@ def decode(q, k_cache, v_cache, scale=None, num_splits=0, out=None, lse=None,
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    need = fa_decode_workspace_size(B, Hq, d, S)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_out("out", out, torch.bfloat16, (B, Hq, d), q)
+    _check_out("lse", lse, torch.float32, (B, Hq), q)
+    workspace, ws_bytes = _workspace(workspace, fa_decode_workspace_size(B, Hq, d, S), q)
     rc = fa_decode_splitkv(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                            out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nk, d,
-                           float(scale), S, workspace.data_ptr(), workspace.numel(),
+                           float(scale), S, workspace.data_ptr(), ws_bytes,
                            _stream_ptr())
     if rc != FA_OK:
         raise FAError(rc, "fa_decode_splitkv")
@@ -314,12 +345,10 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, workspace=None):
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    need = fa_bwd_workspace_size(B, Hq, Nq)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(workspace, fa_bwd_workspace_size(B, Hq, Nq), q)
     rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq,
-                Nk, d, float(scale), int(bool(causal)), workspace.data_ptr(), workspace.numel(),
+                Nk, d, float(scale), int(bool(causal)), workspace.data_ptr(), ws_bytes,
                 _stream_ptr())
     if rc != FA_OK:
         raise FAError(rc, "fa_bwd")
@@ -355,12 +384,12 @@ def decode_serve(q, k_cache, v_cache, seqlens=None, causal=False, scale=None, nu
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    need = fa_decode_serve_workspace_size(B, Hq, Nq, d, S)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_out("out", out, torch.bfloat16, (B, Hq, Nq, d), q)
+    _check_out("lse", lse, torch.float32, (B, Hq, Nq), q)
+    workspace, ws_bytes = _workspace(workspace, fa_decode_serve_workspace_size(B, Hq, Nq, d, S), q)
     rc = fa_decode_serve(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), sl or None,
                          out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale),
-                         int(bool(causal)), S, workspace.data_ptr(), workspace.numel(),
+                         int(bool(causal)), S, workspace.data_ptr(), ws_bytes,
                          _stream_ptr())
     if rc != FA_OK:
         raise FAError(rc, "fa_decode_serve")
@@ -386,6 +415,8 @@ def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal=False, scale=None, 
         out = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check_out("out", out, torch.bfloat16, (B, Hq, Nq, d), q)
+    _check_out("lse", lse, torch.float32, (B, Hq, Nq), q)
     descales = (q_descale, k_descale, v_descale)
     if all(isinstance(x, torch.Tensor) for x in descales):
         for name, t in zip(("q_descale", "k_descale", "v_descale"), descales):
@@ -423,13 +454,12 @@ def fp8_quantize(x, signs=None, codes=None, descale=None, workspace=None):
         codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if descale is None:
         descale = torch.empty(1, dtype=torch.float32, device=x.device)
-    need = fa_fp8_quantize_workspace_size(rows, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check_out("codes", codes, torch.uint8, tuple(x.shape), x)
+    _check_out("descale", descale, torch.float32, (1,), x)
+    workspace, ws_bytes = _workspace(workspace, fa_fp8_quantize_workspace_size(rows, d), x)
     rc = fa_fp8_quantize(x.data_ptr(), codes.data_ptr(), descale.data_ptr(),
                          signs.data_ptr() if signs is not None else None, rows, d,
-                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                         _stream_ptr())
+                         workspace.data_ptr(), ws_bytes, _stream_ptr())
     if rc != FA_OK:
         raise FAError(rc, "fa_fp8_quantize")
     return codes, descale

@@ -486,6 +486,14 @@ const char* fa_strerror(int status) {
 
 const char* fa_last_hip_error(void) { return g_hip_error; }
 
+int fa_build_is_serial(void) {
+#ifdef FA_SERIAL_PIPELINE
+  return 1;
+#else
+  return 0;
+#endif
+}
+
 const char* fa_fwd_kernel_name(int d, int causal, int Nq, int Nk) {
   if (causal != 0 && causal != 1) return nullptr;
   if (Nq <= 0 || Nk <= 0) return nullptr;

@@ -289,8 +289,16 @@ const char* fa_strerror(int status);
 /* Text of the last HIP error seen by this host thread ("" if none). */
 const char* fa_last_hip_error(void);
 
+/* 1 for the race-check build of this library (every staged copy into LDS
+ * completes, behind waits and workgroup barriers, before anything else
+ * runs; its outputs must equal the pipelined build's bit for bit), 0 for
+ * the product build. */
+int fa_build_is_serial(void);
+
 /* Kernel symbol names, as a profiler reports them, so a benchmark can
- * confirm which kernel ran.  NULL for an unsupported head dimension or
+ * confirm which kernel ran: [Evolution] §1.1 ("Before comparing versions,
+ * identify the kernel") asks every measurement to record the kernel that
+ * actually executed.  NULL for an unsupported head dimension or
  * invalid sizes.  fa_fwd_kernel_name: the forward kernel fa_fwd launches for
  * these sizes (the tile depends on d and, for d = 128, on the key length).
  * fa_decode_kernel_name: stage 0 = split kernel (depends on the number of

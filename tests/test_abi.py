@@ -363,3 +363,65 @@ def test_fp8_devscale_rejects(kw, code):
     assert fa.fa_fwd_fp8_devscale(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
                                   a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"], a["qd"],
                                   a["kd"], a["vd"], a["causal"], None) == code
+
+
+def test_build_flag_distinguishes_the_race_check_build():
+    # The race tests compare libfa.so with libfa_serial.so bit for bit; that
+    # only tests something if the second library really is the serial build.
+    assert fa.lib().fa_build_is_serial() == 0
+    assert os.path.exists(fa.SERIAL_LIB_PATH), "libfa_serial.so not built"
+    assert fa.load_library(fa.SERIAL_LIB_PATH).fa_build_is_serial() == 1
+
+
+_QUERY = re.compile(r"^\|\s*`(fa_[a-z0-9_]+)`\s*\|\s*`(fa_[a-z0-9_]+_kernel_name)\(([-0-9, ]*)\)`\s*\|",
+                    re.M)
+
+
+def test_profiled_kernels_are_the_ones_the_library_names():
+    """Every committed profile summary lists the kernels its rocprofv3 trace
+    recorded next to the C-ABI query for that workload; the query must name
+    exactly the kernel that was profiled (a benchmark records which kernel
+    ran, and the name must be the one the library launches)."""
+    prof = os.path.join(ROOT, "profiles")
+    files = sorted(f for f in os.listdir(prof) if f.endswith(".md"))
+    assert files, "no profile summaries committed"
+    seen = 0
+    for f in files:
+        text = open(os.path.join(prof, f)).read()
+        rows = _QUERY.findall(text)
+        assert rows, f"{f}: no executed-kernel table"
+        for kernel, query, args in rows:
+            assert query in fa.EXPORTED_SYMBOLS, f"{f}: {query} is not a C-ABI function"
+            vals = [int(a) for a in args.split(",") if a.strip()]
+            got = getattr(fa, query)(*vals)
+            assert got == kernel, f"{f}: {query}({args}) = {got}, trace shows {kernel}"
+            # the kernel's own statistics are in the same summary
+            assert text.count(kernel) >= 2, f"{f}: no statistics for {kernel}"
+            seen += 1
+    assert seen >= 5
+
+
+class _FakeDeviceTensor:
+    """Stand-in for a device tensor: only what the binding's workspace helper
+    reads (no GPU is needed to check the byte count)."""
+
+    def __init__(self, n, itemsize):
+        self.n, self.itemsize = n, itemsize
+        self.is_cuda = True
+        self.device = "cuda:0"
+
+    def numel(self):
+        return self.n
+
+    def element_size(self):
+        return self.itemsize
+
+    def is_contiguous(self):
+        return True
+
+
+def test_workspace_bytes_count_element_size():
+    like = _FakeDeviceTensor(1, 2)
+    for n, item in ((4096, 1), (1024, 4), (512, 8)):
+        t, nbytes = fa._workspace(_FakeDeviceTensor(n, item), 0, like)
+        assert nbytes == n * item

@@ -154,3 +154,26 @@ def test_decode_repeat_runs_are_bit_identical():
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+
+
+def test_decode_float32_workspace_counts_bytes():
+    """A caller's workspace of another element type is sized in bytes: a
+    float32 tensor of exactly workspace_size/4 elements must be accepted and
+    give the same bits as the default uint8 workspace."""
+    import torch
+    fa = _fa()
+    announce("decode float32 workspace")
+    B, Hq, Hkv, Nk, d, S = 2, 8, 2, 3000, 128, 7
+    qb, kb, vb = datagen.gaussian_bf16(77, [(B, Hq, d), (B, Hkv, Nk, d), (B, Hkv, Nk, d)])
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    need = fa.fa_decode_workspace_size(B, Hq, d, S)
+    assert need % 4 == 0
+    ws32 = torch.empty(need // 4, dtype=torch.float32, device="cuda")
+    o1, l1 = fa.decode(q, k, v, num_splits=S, workspace=ws32)
+    o2, l2 = fa.decode(q, k, v, num_splits=S)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+    with pytest.raises(fa.FAError) as ei:
+        fa.decode(q, k, v, num_splits=S, workspace=ws32[:-1])
+    assert ei.value.status == -5

@@ -61,6 +61,10 @@ ODD = [
     (1, 4, 1, 257, 190, 64, False),
     (1, 1, 1, 1, 1, 128, False),
     (1, 8, 8, 300, 300, 128, True),
+    # non-causal with B*Hq divisible by 8: head-major XCD order, query and key tails
+    (1, 8, 4, 300, 1100, 128, False),
+    (1, 8, 2, 1000, 2100, 128, False),
+    (2, 4, 4, 129, 700, 64, False),
 ]
 
 

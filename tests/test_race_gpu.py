@@ -26,8 +26,10 @@ pytestmark = pytest.mark.gpu
 
 @pytest.fixture(scope="module")
 def serial_lib():
-    fa.lib()   # the pipelined build stays loaded as the default
-    return fa.load_library(fa.SERIAL_LIB_PATH)
+    assert fa.lib().fa_build_is_serial() == 0   # the pipelined build stays the default
+    serial = fa.load_library(fa.SERIAL_LIB_PATH)
+    assert serial.fa_build_is_serial() == 1, "libfa_serial.so is not the race-check build"
+    return serial
 
 
 def _bits(t):
