@@ -66,27 +66,42 @@ struct FwdShape {
   static constexpr int KB = BN / 32;      // 32-key blocks per tile (S^T rows)
   static constexpr int DB = D / 32;       // 32-wide d blocks (O^T rows)
   static constexpr int KC = BN / 16;      // 16-key chunks (PV k-steps)
-  static constexpr int RB = D * 2;        // bytes per K or V row in LDS
+  static constexpr int RB = D * 2;        // bytes per K or V row
   static constexpr int CPR = D / 8;       // 16-byte chunks per row
   static constexpr int TILE = BN * RB;    // bytes of one K (or V) tile
   static constexpr int CHUNKS = BN * CPR;
-  static constexpr int BLKS = CHUNKS / 64;              // 1 KB blocks per tile
-  static constexpr int LOADS = (BLKS + NW - 1) / NW;    // wave loads per tile per wave
+  static constexpr int BLKS = CHUNKS / 64;   // 1 KB blocks per tile
+  static constexpr int LOADS = BLKS / NW;    // 1 KB wave loads per tile per wave
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
-  static_assert(CHUNKS % 64 == 0, "whole 1 KB blocks");
+  static_assert(CHUNKS % 64 == 0 && BLKS % NW == 0, "whole 1 KB blocks, shared evenly");
+  static_assert((NW * 64) % BN == 0, "K loads advance by whole chunk columns");
 };
 
-// LDS layouts (16-byte chunk c of row r is stored at chunk c ^ X(r)):
-//  K: X differs for any 16 consecutive rows, so the S^T A-operand reads (16
-//     lanes = 16 consecutive keys, same chunk) spread over all banks.
-//  V: X = 4*(r mod 4) (scaled for short rows), so the transposing reads of
-//     the PV A operand (8 consecutive keys x 4 consecutive chunks) hit every
-//     bank group exactly twice.
-template <int RB>
-__device__ __forceinline__ int k_xor(int r) {
-  if constexpr (RB >= 256) return r & 15;
-  else return (r / (256 / RB)) & (RB / 16 - 1);
+// Compile-time loop (the buffer loads take their immediate offset as a
+// constant).
+template <int I>
+struct Int {
+  static constexpr int value = I;
+};
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(Int<I>{});
+    static_for<I + 1, N>(f);
+  }
 }
+
+// LDS layouts.
+//  K: chunk-column major.  The 16-byte chunk c (d values 8c..8c+7) of key r
+//     sits at byte (c*BN + r)*16, so the S^T A operand of k-step t (lane
+//     (hl, n) reads chunk 2t+hl of key 32kb+n) is one 16-byte read at a
+//     per-lane base plus a constant: 16 consecutive lanes read 256
+//     contiguous bytes, every bank once, and no address arithmetic is left
+//     in the loop.
+//  V: row major, 16-byte chunk c of row r at chunk c ^ X(r), X(r) =
+//     4*(r mod 4) (scaled for short rows), so the transposing reads of the PV
+//     A operand (8 consecutive keys x 4 consecutive chunks) hit every bank
+//     group exactly twice.
 template <int RB>
 __device__ __forceinline__ int v_xor(int r) {
   if constexpr (RB >= 256) return 4 * (r & 3);
@@ -105,26 +120,76 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Issue the wave's share of one K or V tile as direct global -> LDS loads.
-// Wave load i writes 1 KB block (i*NW + wave) of the tile (when the tile has
-// fewer blocks than waves, only the first waves load); lane l of that
-// load fetches the global chunk whose swizzled position is that block's l-th
-// chunk.  Rows past Nk re-read row Nk-1 (finite data; those keys are masked).
-template <int D, int BN, int NW, bool IS_V>
-__device__ __forceinline__ void load_tile(const uint16_t* base, int j0, int Nk, lds_char* tile,
-                                          int wave, int lane) {
+// Raw buffer resource over the `rows` keys of one tile starting at `base`
+// (bf16 [key][D]): reads past the last of those rows return zero instead of
+// touching memory, which covers the key tail and the tiles past the end
+// (rows = 0) without a branch or a per-lane clamp.  Word 3 is gfx9's
+// 32-bit data format for untyped buffer access.
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int rows) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, rows * D * 2,
+                                           0x00020000);
+}
+
+// Issue the wave's share of one tile as direct buffer -> LDS loads.  Each
+// wave load writes one 1 KB block of the LDS tile (lane l its l-th 16-byte
+// chunk) and fetches, per lane, the global chunk that belongs there.  The
+// per-lane part of the global offset is computed once (voff); the part that
+// varies between a wave's loads is the instruction's immediate offset, which
+// the hardware adds to the LDS address as well (M0 + offset + 16*lane), so
+// the LDS base passed in is the block's address minus that offset.
+//  K: wave w writes blocks i*NW + w; block chunk P = blk*64 + l holds chunk
+//     P / BN of key P % BN, so consecutive loads step by NW*64/BN chunk
+//     columns (16 bytes each) in global memory.
+//  V: wave w writes blocks w*LOADS + i; consecutive blocks are 64/CPR rows
+//     (1 KB) apart in global memory and, with a swizzle period dividing
+//     64/CPR rows, share the per-lane chunk permutation; at d = 256 (two rows
+//     per block, period four) even and odd loads have separate per-lane
+//     offsets.
+template <int D, int BN, int NW>
+__device__ __forceinline__ int k_load_voff(int wave, int lane) {
   using S = FwdShape<D, BN, NW, 1>;
-#pragma unroll
-  for (int i = 0; i < S::LOADS; ++i) {
-    const int blk = i * NW + wave;   // uniform across the wave
-    if (S::BLKS % NW != 0 && blk >= S::BLKS) break;
-    const int P = blk * 64 + lane;
-    const int row = P / S::CPR;
-    const int pc = P % S::CPR;
-    const int c = pc ^ (IS_V ? v_xor<S::RB>(row) : k_xor<S::RB>(row));
-    const int key = min(j0 + row, Nk - 1);
-    __builtin_amdgcn_global_load_lds(base + (size_t)key * D + c * 8, tile + blk * 1024, 16, 0, 0);
-  }
+  const int P = wave * 64 + lane;
+  return (P % BN) * S::RB + (P / BN) * 16;
+}
+template <int D, int BN, int NW>
+__device__ __forceinline__ int v_load_voff(int wave, int lane, int i) {
+  using S = FwdShape<D, BN, NW, 1>;
+  const int P = (wave * S::LOADS + i) * 64 + lane;
+  const int r = P / S::CPR;
+  const int c = (P % S::CPR) ^ v_xor<S::RB>(r);
+  return r * S::RB + c * 16 - i * 1024;
+}
+template <int D, int BN, int NW>
+struct VParity {
+  using S = FwdShape<D, BN, NW, 1>;
+  // the swizzle of rows r and r + 64/CPR differs: two per-lane offsets
+  static constexpr bool value = S::RB >= 256 && (64 / S::CPR) % 4 != 0;
+};
+
+template <int D, int BN, int NW>
+__device__ __forceinline__ void load_k(__amdgpu_buffer_rsrc_t rs, lds_char* tile, int wave,
+                                       int voff) {
+  using S = FwdShape<D, BN, NW, 1>;
+  static_for<0, S::LOADS>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    constexpr int imm = i * (NW * 64 / BN) * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(tile + (i * NW + wave) * 1024 - imm), 16,
+        voff, 0, imm, 0);
+  });
+}
+template <int D, int BN, int NW>
+__device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t rs, lds_char* tile, int wave,
+                                       int voff0, int voff1) {
+  using S = FwdShape<D, BN, NW, 1>;
+  static_for<0, S::LOADS>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    const int voff = (VParity<D, BN, NW>::value && (i & 1)) ? voff1 : voff0;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(tile + wave * S::LOADS * 1024), 16, voff, 0,
+        i * 1024, 0);
+  });
 }
 
 template <int D, int BN, int NW, int NQB, bool CAUSAL, bool SKIP_IDLE, bool HEAD_MAJOR>
@@ -182,6 +247,30 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
     const int last_row = min(q0 + S::BM, p.Nq) - 1;
     nkt = min(nkt, (last_row + off) / BN + 1);
   }
+  // Buffer resource of key tile t: its valid rows (none past nkt).
+  auto k_rsrc = [&](int t) {
+    return tile_rsrc<D>(kbase + (size_t)t * BN * D, t < nkt ? min(p.Nk - t * BN, BN) : 0);
+  };
+  auto v_rsrc = [&](int t) {
+    return tile_rsrc<D>(vbase + (size_t)t * BN * D, t < nkt ? min(p.Nk - t * BN, BN) : 0);
+  };
+  const int kvo = k_load_voff<D, BN, NW>(wave, lane);
+  const int vvo0 = v_load_voff<D, BN, NW>(wave, lane, 0);
+  const int vvo1 = VParity<D, BN, NW>::value ? v_load_voff<D, BN, NW>(wave, lane, 1) : vvo0;
+
+  // The V tiles start as zeros: a tail tile leaves its rows past Nk as they
+  // were, and those rows meet probability 0 in the PV product, which only
+  // stays 0 for finite values.
+  {
+    using v4 = unsigned __attribute__((ext_vector_type(4)));
+    constexpr int per = S::TILE / 16 / S::NT;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      *(__attribute__((address_space(3))) v4*)(vb0 + (i * S::NT + tid) * 16) = v4{};
+      *(__attribute__((address_space(3))) v4*)(vb1 + (i * S::NT + tid) * 16) = v4{};
+    }
+    __syncthreads();
+  }
 
   // The wave owns NQB blocks of 32 query rows; block qb is row qw+32qb+n of
   // this lane.  Q of each block is an MFMA B operand: lane (hl, n) holds
@@ -199,15 +288,18 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
     }
   }
 
-  // Per-lane LDS offsets.  K: row n of each 32-key block, chunk (2t+hl)^X.
-  const int koff = n * S::RB;
-  const int kx = k_xor<S::RB>(n);
+  // Per-lane LDS offsets.  K: chunk hl of key n (then + k-step and key block
+  // constants).
+  const int koff = (hl * BN + n) * 16;
   // V (transposing reads): 16-lane group G = lane/16 reads keys
   // 4*hl + (j/4) (+16kc + 8a) at columns 32db + 16*(G&1) + 4*(j&3).
   const int j16 = lane & 15;
   const int vrow = 4 * hl + (j16 >> 2);
   const int vx = v_xor<S::RB>(vrow) >> 2;
   const int voff = vrow * S::RB + 32 * ((lane >> 4) & 1) + 16 * ((j16 & 3) >> 1) + 8 * (j16 & 1);
+  int vaddr[S::DB];
+#pragma unroll
+  for (int db = 0; db < S::DB; ++db) vaddr[db] = voff + 64 * (db ^ vx);
 
   f32x16 oacc[NQB][S::DB];
   float m_run[NQB], l_run[NQB][2];
@@ -228,7 +320,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
 #pragma unroll
       for (int t = 0; t < S::KSTEPS; ++t) {
         const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(
-            kt + kb * 32 * S::RB + koff + (((2 * t + hl) ^ kx) << 4));
+            kt + koff + (2 * t * BN + 32 * kb) * 16);
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
           sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][t], sacc[qb][kb], 0, 0, 0);
@@ -279,7 +371,6 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
   float mnext[NQB];
   auto step = [&](const lds_char* kr, const lds_char* vr, lds_char* kw, lds_char* vw,
                   f32x16 (&sc)[NQB][S::KB], f32x16 (&sn)[NQB][S::KB], int j) {
-    const int j0 = j * BN;
     if (needs_mask(j)) {
       mask_tile(sc, j);
       tile_max(sc, mnext);
@@ -304,9 +395,11 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
         m_run[qb] = m_new[qb];
       }
     }
+    // Tiles past the end get buffer resources of zero rows: the loads then
+    // read nothing, and no branch splits the step.
     FA_STAGE_FENCE();
-    if (j + 2 < nkt) load_tile<D, BN, NW, false>(kbase, j0 + 2 * BN, p.Nk, kw, wave, lane);
-    if (j + 1 < nkt) load_tile<D, BN, NW, true>(vbase, j0 + BN, p.Nk, vw, wave, lane);
+    load_k<D, BN, NW>(k_rsrc(j + 2), kw, wave, kvo);
+    load_v<D, BN, NW>(v_rsrc(j + 1), vw, wave, vvo0, vvo1);
     FA_STAGE_FENCE();
 
     // S^T of tile j+1 (its result is unused after the last tile).  With one
@@ -317,9 +410,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
 
     // With 8 waves per workgroup (the 256-row tiles) and at d = 256, LLVM's
     // instruction group strategy 0 (LDS reads interleaved with the MFMAs)
-    // schedules this section: +2.6% at the long causal prefill, +2.8% at the
-    // causal B=2 H=16 N=4096 shape, +5.6% at d = 256 on that shape.  The
-    // 128-row d = 128 tile measured -1% with it and d = 64 -3.8%.
+    // schedules this section.
     if constexpr (NW == 8 || D == 256) __builtin_amdgcn_iglp_opt(0);
     // Per 16-key chunk kc: probabilities P = 2^(S*c - m) become the bf16 B
     // operand (registers 8*(kc%2).. of block kc/2), then O^T += V^T P^T for
@@ -345,11 +436,11 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
       }
 #pragma unroll
       for (int db = 0; db < S::DB; ++db) {
-        const int dbo = voff + 64 * (db ^ vx) + 16 * kc * S::RB;
+        const lds_char* va = vr + vaddr[db] + 16 * kc * S::RB;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(vr + dbo));
+            (__attribute__((address_space(3))) s16x4*)(va));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(vr + dbo + 8 * S::RB));
+            (__attribute__((address_space(3))) s16x4*)(va + 8 * S::RB));
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
@@ -365,9 +456,9 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
   // Prologue: K_0, V_0, K_1 to LDS, S^T of tile 0 and its row maximum, then
   // a barrier so that the first step may overwrite K_0's buffer.
   f32x16 sa[NQB][S::KB], sb[NQB][S::KB];   // sb unused without pipelining (see step)
-  load_tile<D, BN, NW, false>(kbase, 0, p.Nk, kb0, wave, lane);
-  load_tile<D, BN, NW, true>(vbase, 0, p.Nk, vb0, wave, lane);
-  if (nkt > 1) load_tile<D, BN, NW, false>(kbase, BN, p.Nk, kb1, wave, lane);
+  load_k<D, BN, NW>(k_rsrc(0), kb0, wave, kvo);
+  load_v<D, BN, NW>(v_rsrc(0), vb0, wave, vvo0, vvo1);
+  load_k<D, BN, NW>(k_rsrc(1), kb1, wave, kvo);
   __syncthreads();
   s_tile(kb0, sa);
   tile_max(sa, mnext);
@@ -391,8 +482,8 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
   }
   auto idle_step = [&](lds_char* kw, lds_char* vw, int j) {
     FA_STAGE_FENCE();
-    if (j + 2 < nkt) load_tile<D, BN, NW, false>(kbase, (j + 2) * BN, p.Nk, kw, wave, lane);
-    if (j + 1 < nkt) load_tile<D, BN, NW, true>(vbase, (j + 1) * BN, p.Nk, vw, wave, lane);
+    load_k<D, BN, NW>(k_rsrc(j + 2), kw, wave, kvo);
+    load_v<D, BN, NW>(v_rsrc(j + 1), vw, wave, vvo0, vvo1);
     FA_STAGE_FENCE();
     __syncthreads();
   };
@@ -402,6 +493,8 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
     idle_step(kb0, vb1, j);
     if (j + 1 < nkt) idle_step(kb1, vb0, j + 1);
   }
+  // No load into this workgroup's LDS may still be in flight when it ends.
+  __builtin_amdgcn_s_waitcnt(0);
 
   // Epilogue: O = acc / l (bf16, round to nearest even), LSE in natural log.
 #pragma unroll
