@@ -70,11 +70,15 @@ struct FwdShape {
   static constexpr int CPR = D / 8;       // 16-byte chunks per row
   static constexpr int TILE = BN * RB;    // bytes of one K (or V) tile
   static constexpr int CHUNKS = BN * CPR;
-  static constexpr int BLKS = CHUNKS / 64;   // 1 KB blocks per tile
-  static constexpr int LOADS = BLKS / NW;    // 1 KB wave loads per tile per wave
+  static constexpr int BLKS = CHUNKS / 64;   // 1 KB blocks per V tile
+  static constexpr int LOADS = BLKS / NW;    // 1 KB wave loads per V tile per wave
+  // K rows are padded by one 16-byte chunk in LDS (see below).
+  static constexpr int KRB = RB + 16;                   // bytes per K row in LDS
+  static constexpr int KBLKS = (BN * (CPR + 1) + 63) / 64;   // 1 KB blocks per K tile
+  static constexpr int KLOADS = (KBLKS + NW - 1) / NW;  // K wave loads per tile per wave
+  static constexpr int KTILE = KLOADS * NW * 1024;      // LDS bytes per K buffer
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
   static_assert(CHUNKS % 64 == 0 && BLKS % NW == 0, "whole 1 KB blocks, shared evenly");
-  static_assert((NW * 64) % BN == 0, "K loads advance by whole chunk columns");
 };
 
 // Compile-time loop (the buffer loads take their immediate offset as a
@@ -92,12 +96,12 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // LDS layouts.
-//  K: chunk-column major.  The 16-byte chunk c (d values 8c..8c+7) of key r
-//     sits at byte (c*BN + r)*16, so the S^T A operand of k-step t (lane
-//     (hl, n) reads chunk 2t+hl of key 32kb+n) is one 16-byte read at a
-//     per-lane base plus a constant: 16 consecutive lanes read 256
-//     contiguous bytes, every bank once, and no address arithmetic is left
-//     in the loop.
+//  K: row major with rows padded to RB + 16 bytes, so that row r starts 4
+//     banks after row r - 1: the S^T A operand of k-step t (lane (hl, n)
+//     reads chunk 2t+hl of key 32kb+n) touches every bank once per 16
+//     lanes, and its address is a per-lane base plus a constant, with no
+//     address arithmetic left in the loop.  The global loads stay coalesced
+//     (each 1 KB block holds about four consecutive rows).
 //  V: row major, 16-byte chunk c of row r at chunk c ^ X(r), X(r) =
 //     4*(r mod 4) (scaled for short rows), so the transposing reads of the PV
 //     A operand (8 consecutive keys x 4 consecutive chunks) hit every bank
@@ -134,23 +138,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base
 // Issue the wave's share of one tile as direct buffer -> LDS loads.  Each
 // wave load writes one 1 KB block of the LDS tile (lane l its l-th 16-byte
 // chunk) and fetches, per lane, the global chunk that belongs there.  The
-// per-lane part of the global offset is computed once (voff); the part that
-// varies between a wave's loads is the instruction's immediate offset, which
-// the hardware adds to the LDS address as well (M0 + offset + 16*lane), so
-// the LDS base passed in is the block's address minus that offset.
-//  K: wave w writes blocks i*NW + w; block chunk P = blk*64 + l holds chunk
-//     P / BN of key P % BN, so consecutive loads step by NW*64/BN chunk
-//     columns (16 bytes each) in global memory.
+// per-lane global offsets are computed once.  The instruction's immediate
+// offset is added to the LDS address as well as the global one (M0 +
+// offset + 16*lane), so the LDS base passed in is the block's address minus
+// that offset.
+//  K: wave w writes blocks i*NW + w.  Block chunk P = blk*64 + l is slot
+//     P % (CPR+1) of row P / (CPR+1); the padding slot re-reads the row's
+//     first chunk.  The offsets differ between a wave's loads, one register
+//     each.  Blocks past the tile (when NW does not divide the block count)
+//     read through a resource of zero rows into the buffer's spare space.
 //  V: wave w writes blocks w*LOADS + i; consecutive blocks are 64/CPR rows
 //     (1 KB) apart in global memory and, with a swizzle period dividing
 //     64/CPR rows, share the per-lane chunk permutation; at d = 256 (two rows
 //     per block, period four) even and odd loads have separate per-lane
 //     offsets.
 template <int D, int BN, int NW>
-__device__ __forceinline__ int k_load_voff(int wave, int lane) {
+__device__ __forceinline__ int k_load_voff(int wave, int lane, int i) {
   using S = FwdShape<D, BN, NW, 1>;
-  const int P = wave * 64 + lane;
-  return (P % BN) * S::RB + (P / BN) * 16;
+  const int P = (i * NW + wave) * 64 + lane;
+  const int r = P / (S::CPR + 1);
+  const int slot = P % (S::CPR + 1);
+  return min(r, BN - 1) * S::RB + (slot < S::CPR ? slot : 0) * 16;
 }
 template <int D, int BN, int NW>
 __device__ __forceinline__ int v_load_voff(int wave, int lane, int i) {
@@ -168,15 +176,15 @@ struct VParity {
 };
 
 template <int D, int BN, int NW>
-__device__ __forceinline__ void load_k(__amdgpu_buffer_rsrc_t rs, lds_char* tile, int wave,
-                                       int voff) {
+__device__ __forceinline__ void load_k(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rs0,
+                                       lds_char* tile, int wave, const int* voff) {
   using S = FwdShape<D, BN, NW, 1>;
-  static_for<0, S::LOADS>([&](auto ic) {
+  static_for<0, S::KLOADS>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
-    constexpr int imm = i * (NW * 64 / BN) * 16;
+    const bool live = (S::KBLKS % NW == 0) || i * NW + wave < S::KBLKS;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (__attribute__((address_space(3))) void*)(tile + (i * NW + wave) * 1024 - imm), 16,
-        voff, 0, imm, 0);
+        live ? rs : rs0, (__attribute__((address_space(3))) void*)(tile + (i * NW + wave) * 1024),
+        16, voff[i], 0, 0, 0);
   });
 }
 template <int D, int BN, int NW>
@@ -189,6 +197,35 @@ __device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t rs, lds_char* tile
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rs, (__attribute__((address_space(3))) void*)(tile + wave * S::LOADS * 1024), 16, voff, 0,
         i * 1024, 0);
+  });
+}
+
+// Instruction order of one pipelined step (one 32-row block per wave, the
+// next tile's S^T beside this tile's softmax): the wave's tile loads first,
+// then every MFMA followed by its share of the LDS operand reads (issued
+// PRE MFMAs ahead of their use) and of the softmax VALU work, so that each
+// wave alone keeps the matrix pipe fed and the VALU busy beside it.  Three
+// VALU instructions follow each S^T MFMA and five each PV MFMA: the
+// probabilities of the first chunks are ready before the first PV product.
+// Measured at the long causal prefill: +2.4% over LLVM's strategy 0.
+template <typename S>
+__device__ __forceinline__ void sched_step() {
+  constexpr int PRE = 6;
+  constexpr int NS = S::KSTEPS * S::KB;   // S^T MFMAs (one K read each)
+  constexpr int NP = S::KC * S::DB;       // PV MFMAs (two V reads each)
+  __builtin_amdgcn_sched_group_barrier(0x020, S::LOADS + S::KLOADS, 0);   // buffer loads
+  __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);                    // LDS reads
+  static_for<0, NS>([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, m < NS - PRE ? 1 : 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);                    // VALU
+  });
+  static_for<0, NP>([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, m < NP - PRE ? 2 : 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
   });
 }
 
@@ -254,7 +291,10 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
   auto v_rsrc = [&](int t) {
     return tile_rsrc<D>(vbase + (size_t)t * BN * D, t < nkt ? min(p.Nk - t * BN, BN) : 0);
   };
-  const int kvo = k_load_voff<D, BN, NW>(wave, lane);
+  int kvo[S::KLOADS];
+#pragma unroll
+  for (int i = 0; i < S::KLOADS; ++i) kvo[i] = k_load_voff<D, BN, NW>(wave, lane, i);
+  __amdgpu_buffer_rsrc_t no_rows = tile_rsrc<D>(kbase, 0);
   const int vvo0 = v_load_voff<D, BN, NW>(wave, lane, 0);
   const int vvo1 = VParity<D, BN, NW>::value ? v_load_voff<D, BN, NW>(wave, lane, 1) : vvo0;
 
@@ -290,7 +330,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
 
   // Per-lane LDS offsets.  K: chunk hl of key n (then + k-step and key block
   // constants).
-  const int koff = (hl * BN + n) * 16;
+  const int koff = n * S::KRB + hl * 16;
   // V (transposing reads): 16-lane group G = lane/16 reads keys
   // 4*hl + (j/4) (+16kc + 8a) at columns 32db + 16*(G&1) + 4*(j&3).
   const int j16 = lane & 15;
@@ -314,13 +354,17 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
   // S^T = K Q^T for one tile; every K operand read from LDS feeds NQB MFMAs.
   auto s_tile = [&](const lds_char* kt, f32x16 (&sacc)[NQB][S::KB]) {
 #pragma unroll
-    for (int kb = 0; kb < S::KB; ++kb) {
+    for (int kb = 0; kb < S::KB; ++kb)
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) sacc[qb][kb] = f32x16{};
+    // k-step outer, key block inner: consecutive MFMAs accumulate into
+    // different registers.
 #pragma unroll
-      for (int t = 0; t < S::KSTEPS; ++t) {
+    for (int t = 0; t < S::KSTEPS; ++t) {
+#pragma unroll
+      for (int kb = 0; kb < S::KB; ++kb) {
         const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(
-            kt + koff + (2 * t * BN + 32 * kb) * 16);
+            kt + koff + 32 * t + 32 * kb * S::KRB);
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
           sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][t], sacc[qb][kb], 0, 0, 0);
@@ -398,7 +442,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
     // Tiles past the end get buffer resources of zero rows: the loads then
     // read nothing, and no branch splits the step.
     FA_STAGE_FENCE();
-    load_k<D, BN, NW>(k_rsrc(j + 2), kw, wave, kvo);
+    load_k<D, BN, NW>(k_rsrc(j + 2), no_rows, kw, wave, kvo);
     load_v<D, BN, NW>(v_rsrc(j + 1), vw, wave, vvo0, vvo1);
     FA_STAGE_FENCE();
 
@@ -408,10 +452,10 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
     // products keeps a single S^T tile live.
     if constexpr (kPipe) s_tile(kr, sn);
 
-    // With 8 waves per workgroup (the 256-row tiles) and at d = 256, LLVM's
-    // instruction group strategy 0 (LDS reads interleaved with the MFMAs)
-    // schedules this section.
-    if constexpr (NW == 8 || D == 256) __builtin_amdgcn_iglp_opt(0);
+    // At d = 256, LLVM's instruction group strategy 0 (LDS reads interleaved
+    // with the MFMAs) schedules this section; the 8-wave d = 128 tile has an
+    // explicit schedule (below).
+    if constexpr (D == 256) __builtin_amdgcn_iglp_opt(0);
     // Per 16-key chunk kc: probabilities P = 2^(S*c - m) become the bf16 B
     // operand (registers 8*(kc%2).. of block kc/2), then O^T += V^T P^T for
     // every d block, the V^T operand coming from two transposing reads and
@@ -450,15 +494,16 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
 
     if constexpr (!kPipe) s_tile(kr, sn);
     tile_max(sn, mnext);
+    if constexpr (NW == 8 && D == 128) sched_step<S>();
     __syncthreads();
   };
 
   // Prologue: K_0, V_0, K_1 to LDS, S^T of tile 0 and its row maximum, then
   // a barrier so that the first step may overwrite K_0's buffer.
   f32x16 sa[NQB][S::KB], sb[NQB][S::KB];   // sb unused without pipelining (see step)
-  load_k<D, BN, NW>(k_rsrc(0), kb0, wave, kvo);
+  load_k<D, BN, NW>(k_rsrc(0), no_rows, kb0, wave, kvo);
   load_v<D, BN, NW>(v_rsrc(0), vb0, wave, vvo0, vvo1);
-  load_k<D, BN, NW>(k_rsrc(1), kb1, wave, kvo);
+  load_k<D, BN, NW>(k_rsrc(1), no_rows, kb1, wave, kvo);
   __syncthreads();
   s_tile(kb0, sa);
   tile_max(sa, mnext);
@@ -482,7 +527,7 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
   }
   auto idle_step = [&](lds_char* kw, lds_char* vw, int j) {
     FA_STAGE_FENCE();
-    load_k<D, BN, NW>(k_rsrc(j + 2), kw, wave, kvo);
+    load_k<D, BN, NW>(k_rsrc(j + 2), no_rows, kw, wave, kvo);
     load_v<D, BN, NW>(v_rsrc(j + 1), vw, wave, vvo0, vvo1);
     FA_STAGE_FENCE();
     __syncthreads();
@@ -529,8 +574,8 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
   extern "C" __global__ void __launch_bounds__(64 * NW, WAVES_PER_EU) NAME(           \
       fa::FwdParams p) {                                                              \
     using Sh = fa::FwdShape<D, BN, NW, NQB>;                                          \
-    __shared__ __attribute__((aligned(1024))) char k0[Sh::TILE];                      \
-    __shared__ __attribute__((aligned(1024))) char k1[Sh::TILE];                      \
+    __shared__ __attribute__((aligned(1024))) char k0[Sh::KTILE];                     \
+    __shared__ __attribute__((aligned(1024))) char k1[Sh::KTILE];                     \
     __shared__ __attribute__((aligned(1024))) char v0[Sh::TILE];                      \
     __shared__ __attribute__((aligned(1024))) char v1[Sh::TILE];                      \
     fa::fwd_body<D, BN, NW, NQB, CAUSAL, SKIP_IDLE, HEAD_MAJOR>(p, (fa::lds_char*)k0,  \
