@@ -22,7 +22,8 @@ __all__ = [
     "fa_decode_serve", "fa_decode_serve_workspace_size", "fa_decode_serve_num_splits",
     "fa_decode_serve_kernel_name", "fa_fwd_fp8", "fa_fwd_fp8_kernel_name",
     "fa_fwd_fp8_devscale", "fa_fp8_quantize", "fa_fp8_quantize_workspace_size",
-    "fa_fp8_quantize_kernel_name", "fa_build_is_serial",
+    "fa_fp8_quantize_kernel_name", "fa_build_is_serial", "fa_decode_splitkv_noalloc",
+    "DECODE_NOALLOC_SCRATCH_BYTES", "decode_noalloc",
     "fwd", "fwd_fp8", "fp8_quantize", "decode", "decode_serve", "bwd", "EXPORTED_SYMBOLS",
     "LIB_PATH", "SERIAL_LIB_PATH", "load_library",
 ]
@@ -70,7 +71,13 @@ _SIGNATURES = {
     "fa_fp8_quantize": (_i, [_vp, _vp, _vp, _vp, _i, _i, _vp, _sz, _vp]),
     "fa_fp8_quantize_kernel_name": (_cs, [_i, _i]),
     "fa_build_is_serial": (_i, []),
+    "fa_decode_splitkv_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
+                                       _vp]),
 }
+
+# FA_DECODE_NOALLOC_SCRATCH_BYTES of include/fa.h: the fixed scratch of
+# fa_decode_splitkv_noalloc.
+DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
 _lib = None
@@ -122,6 +129,12 @@ def fa_decode_splitkv(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nk, d, scale,
     return lib().fa_decode_splitkv(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nk, d,
                                    scale, num_splits, workspace, workspace_bytes,
                                    stream)
+
+
+def fa_decode_splitkv_noalloc(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nk, d, scale,
+                              num_splits, stream=None):
+    return lib().fa_decode_splitkv_noalloc(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nk, d,
+                                           scale, num_splits, stream)
 
 
 def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale, causal,
@@ -323,6 +336,30 @@ def decode(q, k_cache, v_cache, scale=None, num_splits=0, out=None, lse=None,
                            _stream_ptr())
     if rc != FA_OK:
         raise FAError(rc, "fa_decode_splitkv")
+    return out, lse
+
+
+def decode_noalloc(q, k_cache, v_cache, out, lse, scale=None, num_splits=0):
+    """Split-KV decode through the allocation-free entry point: the caller
+    passes the outputs (out bf16 [B][Hq][d], lse fp32 [B][Hq]) and nothing is
+    allocated; the split partials live in the library's fixed scratch."""
+    import torch
+    _check_bf16("q", q, 3)
+    _check_bf16("k_cache", k_cache, 4)
+    _check_bf16("v_cache", v_cache, 4)
+    B, Hq, d = q.shape
+    Hkv, Nk = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, Nk, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("caches must be [B][Hkv][Nk][d] with q's B and d")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check_out("out", out, torch.bfloat16, (B, Hq, d), q)
+    _check_out("lse", lse, torch.float32, (B, Hq), q)
+    rc = fa_decode_splitkv_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                   out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nk, d,
+                                   float(scale), num_splits, _stream_ptr())
+    if rc != FA_OK:
+        raise FAError(rc, "fa_decode_splitkv_noalloc")
     return out, lse
 
 

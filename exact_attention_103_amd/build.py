@@ -22,7 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
 SERIAL_LIB = os.path.join(PKG, "libfa_serial.so")
 
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_fp8_quant.hip", "fa_decode.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_fp8_quant.hip", "fa_decode.hip", "fa_bwd.hip",
+           "fa_noalloc.hip"]
 
 # Packed fp32 VALU forms are switched off for the device code; hipcc's host
 # pass warns that it does not know the feature, which is harmless.

@@ -117,6 +117,47 @@ int fwd_fp8_common(const void* q, const void* k, const void* v, void* o, float* 
 
 }  // namespace
 
+// Shared with the allocation-free decode (fa_noalloc.hip).
+namespace fa {
+
+int decode_check(const void* q, const void* k_cache, const void* v_cache, const void* o,
+                 const float* lse, int B, int Hq, int Hkv, int Nk, int d, float scale,
+                 int num_splits, int* splits) {
+  if (!q || !k_cache || !v_cache || !o || !lse) return FA_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nk <= 0) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (!supported_d(d)) return FA_ERR_HEAD_DIM;
+  if (!scale_ok(scale)) return FA_ERR_SCALE;
+  if (num_splits < 0 || num_splits > max_splits(Nk)) return FA_ERR_SPLITS;
+  const int S = num_splits == 0 ? fa_decode_num_splits(B, Hq, Hkv, Nk, d) : num_splits;
+  if (S < 0) return S;
+  if (fa_decode_workspace_size(B, Hq, d, S) == 0) return FA_ERR_TOO_LARGE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+      !aligned16(lse))
+    return FA_ERR_ALIGN;
+
+  const int group = Hq / Hkv;
+  const int64_t q_bytes = checked_product({B, Hq, d, 2});
+  const int64_t kv_bytes = checked_product({B, Hkv, Nk, d, 2});
+  const int64_t lse_bytes = checked_product({B, Hq, 4});
+  const int64_t grid = checked_product({B, Hkv, S, group / decode_group_tile(group)});
+  if (q_bytes < 0 || kv_bytes < 0 || lse_bytes < 0 || grid < 0 || grid > INT32_MAX)
+    return FA_ERR_TOO_LARGE;
+
+  const Span sq = span(q, q_bytes), sk = span(k_cache, kv_bytes), sv = span(v_cache, kv_bytes);
+  const Span so = span(o, q_bytes), sl = span(lse, lse_bytes);
+  const Span ins[3] = {sq, sk, sv};
+  for (const Span& in : ins)
+    if (overlaps(so, in) || overlaps(sl, in)) return FA_ERR_ALIAS;
+  if (overlaps(so, sl)) return FA_ERR_ALIAS;
+  *splits = S;
+  return FA_OK;
+}
+
+int hip_status(hipError_t e) { return hip_fail(e); }
+
+}  // namespace fa
+
 extern "C" {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -256,39 +297,24 @@ int fa_decode_num_splits(int B, int Hq, int Hkv, int Nk, int d) {
   return static_cast<int>(s);
 }
 
+
 int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache, void* o,
                       float* lse, int B, int Hq, int Hkv, int Nk, int d, float scale,
                       int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k_cache || !v_cache || !o || !lse) return FA_ERR_NULL;
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nk <= 0) return FA_ERR_SHAPE;
-  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
-  if (!supported_d(d)) return FA_ERR_HEAD_DIM;
-  if (!scale_ok(scale)) return FA_ERR_SCALE;
-  if (num_splits < 0 || num_splits > max_splits(Nk)) return FA_ERR_SPLITS;
-  const int S = num_splits == 0 ? fa_decode_num_splits(B, Hq, Hkv, Nk, d) : num_splits;
-  if (S < 0) return S;
+  int S = 0;
+  const int rc = fa::decode_check(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nk, d, scale,
+                                  num_splits, &S);
+  if (rc != FA_OK) return rc;
   const size_t need = fa_decode_workspace_size(B, Hq, d, S);
-  if (need == 0) return FA_ERR_TOO_LARGE;
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
-      !aligned16(lse) || !aligned16(workspace))
-    return FA_ERR_ALIGN;
-
-  const int group = Hq / Hkv;
-  const int64_t q_bytes = checked_product({B, Hq, d, 2});
-  const int64_t kv_bytes = checked_product({B, Hkv, Nk, d, 2});
-  const int64_t lse_bytes = checked_product({B, Hq, 4});
-  const int64_t grid = checked_product({B, Hkv, S, group / fa::decode_group_tile(group)});
-  if (q_bytes < 0 || kv_bytes < 0 || lse_bytes < 0 || grid < 0 || grid > INT32_MAX)
-    return FA_ERR_TOO_LARGE;
-
-  const Span sq = span(q, q_bytes), sk = span(k_cache, kv_bytes), sv = span(v_cache, kv_bytes);
-  const Span so = span(o, q_bytes), sl = span(lse, lse_bytes);
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  const int64_t q_bytes = static_cast<int64_t>(B) * Hq * d * 2;
+  const int64_t kv_bytes = static_cast<int64_t>(B) * Hkv * Nk * d * 2;
   const Span sw = span(workspace, static_cast<int64_t>(need));
-  const Span ins[3] = {sq, sk, sv};
-  for (const Span& in : ins)
-    if (overlaps(so, in) || overlaps(sl, in) || overlaps(sw, in)) return FA_ERR_ALIAS;
-  if (overlaps(so, sl) || overlaps(so, sw) || overlaps(sl, sw)) return FA_ERR_ALIAS;
+  const Span others[5] = {span(q, q_bytes), span(k_cache, kv_bytes), span(v_cache, kv_bytes),
+                          span(o, q_bytes), span(lse, static_cast<int64_t>(B) * Hq * 4)};
+  for (const Span& t : others)
+    if (overlaps(sw, t)) return FA_ERR_ALIAS;
 
   fa::DecodeParams p;
   p.q = static_cast<const uint16_t*>(q);
@@ -302,7 +328,7 @@ int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache, v
   p.Hq = Hq;
   p.Hkv = Hkv;
   p.Nk = Nk;
-  p.group = group;
+  p.group = Hq / Hkv;
   p.splits = S;
   p.chunk = split_chunk(Nk, S);
   p.c = scale * fa::kLog2e;
@@ -480,6 +506,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA_ERR_TOO_LARGE: return "sizes exceed the supported range";
+    case FA_ERR_SCRATCH: return "the split partials exceed the fixed scratch of the allocation-free decode";
     default: return "unknown status";
   }
 }

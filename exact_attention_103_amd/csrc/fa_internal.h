@@ -169,4 +169,16 @@ int decode_group_tile(int group);
 // Keys per decode split are rounded up to this multiple.
 constexpr int kDecodeChunkAlign = 64;
 
+// Every check fa_decode_splitkv makes except those on the workspace (nulls,
+// shapes, head dim, scale, split range, alignment, size limits, overlaps
+// among the tensors), with no HIP call; on FA_OK *splits is the split count
+// after the 0 -> heuristic substitution.
+int decode_check(const void* q, const void* k_cache, const void* v_cache, const void* o,
+                 const float* lse, int B, int Hq, int Hkv, int Nk, int d, float scale,
+                 int num_splits, int* splits);
+
+// Records the text of a HIP error for fa_last_hip_error and returns
+// FA_ERR_HIP.
+int hip_status(hipError_t e);
+
 }  // namespace fa

@@ -13,8 +13,10 @@
  * Conventions shared by every entry point
  *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
  *     allocates no memory and keeps no state between calls (apart from the
- *     thread-local text of the last HIP error).  Calls from several host
- *     threads are safe.
+ *     thread-local text of the last HIP error, and the fixed scratch array of
+ *     fa_decode_splitkv_noalloc with its per-device address).  Calls from
+ *     several host threads are safe, except overlapping calls of
+ *     fa_decode_splitkv_noalloc on one GPU.
  *   - Layout: [B][H][N][d] contiguous, d fastest, bf16 (IEEE bfloat16 bit
  *     patterns in 16-bit words).  LSE is fp32.  Every tensor pointer must be
  *     16-byte aligned.
@@ -23,6 +25,8 @@
  *     kernel surfaces at the caller's next synchronisation.
  *   - Every argument check runs before any HIP call.  On a negative return
  *     nothing was enqueued and no output byte was written.
+ *   - Every kernel-side scratch buffer is a caller workspace argument, except
+ *     in fa_decode_splitkv_noalloc.
  *   - Results are deterministic: no atomics, fixed reduction order.
  *   - Non-finite inputs are not checked; the result is then undefined.
  */
@@ -48,7 +52,9 @@ enum fa_status {
   FA_ERR_HIP = -7,        /* a HIP launch failed; see fa_last_hip_error()    */
   FA_ERR_SCALE = -8,      /* scale not finite or not > 0                     */
   FA_ERR_ALIAS = -9,      /* an output overlaps an input or another output   */
-  FA_ERR_TOO_LARGE = -10  /* sizes exceed the 2^31 grid / 2^62 byte limits   */
+  FA_ERR_TOO_LARGE = -10, /* sizes exceed the 2^31 grid / 2^62 byte limits   */
+  FA_ERR_SCRATCH = -11    /* fa_decode_splitkv_noalloc: the partials need more
+                             than FA_DECODE_NOALLOC_SCRATCH_BYTES            */
 };
 
 /*
@@ -191,6 +197,35 @@ int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                       void* o, float* lse, int B, int Hq, int Hkv, int Nk,
                       int d, float scale, int num_splits, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * fa_decode_splitkv_noalloc -- fa_decode_splitkv without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * stream capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * The split partials go to a fixed array inside the library of
+ * FA_DECODE_NOALLOC_SCRATCH_BYTES (16 MiB), which every GPU the library runs
+ * on holds from the library's load until the process ends.  The call
+ * allocates nothing and frees nothing.  The first call on a device looks up
+ * that device's copy of the array (with the device current); later calls
+ * reuse the address.
+ *
+ * Arguments, results and errors as fa_decode_splitkv, plus FA_ERR_SCRATCH
+ * when fa_decode_workspace_size(B, Hq, d, splits) exceeds
+ * FA_DECODE_NOALLOC_SCRATCH_BYTES (e.g. B = 8, Hq = 32, d = 128 allows up to
+ * 127 splits).  `stream` must belong to the current device (else FA_ERR_HIP).
+ * Outputs equal fa_decode_splitkv's bit for bit for the same split count.
+ *
+ * Every call on one GPU shares that GPU's array, and the array keeps the last
+ * call's contents (nothing needs clearing: each call writes every partial it
+ * reads).  Calls that can overlap on one GPU -- on different streams, or
+ * from different host threads -- race on it; serialise them (one stream, or
+ * events between the streams).
+ */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES (16u << 20)
+int fa_decode_splitkv_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              void* o, float* lse, int B, int Hq, int Hkv, int Nk, int d,
+                              float scale, int num_splits, void* stream);
 
 /*
  * fa_decode_serve -- serving-shaped split-KV decode: Nq (1..16) query rows

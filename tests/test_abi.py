@@ -223,6 +223,43 @@ def test_decode_rejects(kw, code):
     assert _dec(**kw) == code
 
 
+def _dec_noalloc(**kw):
+    a = dict(GOOD_DEC)
+    a.update(kw)
+    return fa.fa_decode_splitkv_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"],
+                                        a["Hq"], a["Hkv"], a["Nk"], a["d"], a["scale"],
+                                        a["S"], None)
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), -1), (dict(lse=0), -1),
+    (dict(B=0), -2), (dict(Hq=6, Hkv=4), -2), (dict(Nk=0), -2),
+    (dict(d=100), -3),
+    (dict(q=Q + 2), -4), (dict(o=O + 8), -4),
+    (dict(S=-1), -6), (dict(S=17), -6),
+    (dict(scale=float("nan")), -8),
+    (dict(o=K + 64), -9), (dict(lse=O), -9),
+    # 4*B*Hq*S*(d+1) bytes of partials: 8*32 heads at d = 128 fit 127 splits
+    # in 16 MiB, not 128.
+    (dict(B=8, Hq=32, Hkv=8, Nk=32768, S=128, k=1 << 40, v=2 << 40, o=3 << 40, lse=4 << 40),
+     -11),
+    (dict(B=1 << 20, Hq=1 << 11, Hkv=1 << 11, Nk=1 << 20, S=1), -10),
+])
+def test_decode_noalloc_rejects(kw, code):
+    # Every one of these returns before any HIP call.
+    assert _dec_noalloc(**kw) == code
+
+
+def test_decode_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+FA_DECODE_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", text)
+    assert m, "FA_DECODE_NOALLOC_SCRATCH_BYTES not found"
+    assert int(m.group(1)) << int(m.group(2)) == fa.DECODE_NOALLOC_SCRATCH_BYTES
+    assert fa.fa_decode_workspace_size(8, 32, 128, 127) <= fa.DECODE_NOALLOC_SCRATCH_BYTES
+    assert fa.fa_decode_workspace_size(8, 32, 128, 128) > fa.DECODE_NOALLOC_SCRATCH_BYTES
+
+
 @cpu_only
 def test_decode_exact_workspace_is_enough_and_heuristic_checked():
     # S = 4: need 4*B*Hq*S*(d+1) bytes; one byte short fails, exact size would
