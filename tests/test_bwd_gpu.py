@@ -7,7 +7,9 @@ the GPU forward first and feed its O and LSE to the backward, as a training
 step does, and compare sampled heads, rows and keys against the oracle
 gradients of the same q, k, v, dO.  The bar (tests/parity.py) is a relative
 Frobenius error <= 1e-2 and a largest error <= 3e-2 of the largest reference
-magnitude, per gradient.
+magnitude, per gradient, and for every compared element an error bound
+derived from the kernels' bf16 and fp32 roundings (grad_error_bounds), given
+the O and LSE the backward was fed.
 """
 
 import numpy as np
@@ -15,7 +17,8 @@ import pytest
 
 import datagen
 import oracle
-from parity import announce, assert_grad_parity, dev_bf16, host_f64
+from parity import (announce, assert_grad_parity, dev_bf16, grad_error_bounds,
+                    head_grad_error_bounds, host_f64)
 
 import exact_attention_103_amd as fa
 
@@ -66,8 +69,10 @@ def test_bwd_full_parity(shape):
     ob, lse32 = _oracle_fwd_outputs(q64, k64, v64, cfg.scale, causal)
     dq, dk, dv = _bwd_on_gpu(qb, kb, vb, dob, ob, lse32, cfg.scale, causal)
     rq, rk, rv = oracle.attention_bwd_ref(q64, k64, v64, do64, cfg.scale, causal)
-    assert_grad_parity(tag, dict(Q=host_f64(dq), K=host_f64(dk), V=host_f64(dv)),
-                       dict(Q=rq, K=rk, V=rv))
+    refs = dict(Q=rq, K=rk, V=rv)
+    bounds = grad_error_bounds(q64, k64, v64, do64, datagen.f64_from_bf16_bits(ob),
+                               lse32.astype(np.float64), cfg.scale, causal, refs)
+    assert_grad_parity(tag, dict(Q=host_f64(dq), K=host_f64(dk), V=host_f64(dv)), refs, bounds)
 
 
 def _workload_case(name, heads, rows_per_head=None, keys_per_head=None):
@@ -81,6 +86,7 @@ def _workload_case(name, heads, rows_per_head=None, keys_per_head=None):
     o, lse = fa.fwd(q, k, v, causal=cfg.causal, scale=cfg.scale)
     dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=cfg.causal, scale=cfg.scale)
     torch.cuda.synchronize()
+    assert cfg.Hq == cfg.Hkv, "the sampled comparison reads one query head per KV head"
     for b, h in heads:
         g = h // (cfg.Hq // cfg.Hkv)
         rows = None if rows_per_head is None else datagen.row_subset(cfg.Nq, rows_per_head, h)
@@ -96,7 +102,11 @@ def _workload_case(name, heads, rows_per_head=None, keys_per_head=None):
             gq = gq[rows]
         if keys is not None:
             gk, gv = gk[keys], gv[keys]
-        assert_grad_parity(f"{name} b{b} h{h}", dict(Q=gq, K=gk, V=gv), dict(Q=rq, K=rk, V=rv))
+        refs = dict(Q=rq, K=rk, V=rv)
+        bounds = head_grad_error_bounds(sel(qb, b, h), sel(kb, b, g), sel(vb, b, g),
+                                        sel(dob, b, h), host_f64(o[b, h]), host_f64(lse[b, h]),
+                                        cfg.scale, cfg.causal, refs, rows=rows, keys=keys)
+        assert_grad_parity(f"{name} b{b} h{h}", dict(Q=gq, K=gk, V=gv), refs, bounds)
 
 
 def test_bwd_train_noncausal_sampled():
