@@ -498,7 +498,7 @@ const char* fa_strerror(int status) {
     case FA_OK: return "success";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid shape (sizes must be > 0, Hq a multiple of Hkv, causal needs Nq <= Nk)";
-    case FA_ERR_HEAD_DIM: return "unsupported head dimension (32, 64, 128 or 256; backward: 32, 64 or 128)";
+    case FA_ERR_HEAD_DIM: return "unsupported head dimension (32, 64, 128 or 256; fp8 forward: 64 or 128)";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case FA_ERR_WORKSPACE: return "workspace is NULL or too small";
     case FA_ERR_SPLITS: return "num_splits out of range";

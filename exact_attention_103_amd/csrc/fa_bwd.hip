@@ -93,7 +93,10 @@ struct BwdShape {
 
 constexpr int kBwdWaves = 4;
 constexpr int kDqRows = 32 * kBwdWaves;    // query rows per dQ workgroup
-constexpr int kDqKeys = 64;                // keys per K/V tile in the dQ kernel
+// Keys per K/V tile in the dQ kernel: 64, or 32 at d = 256, where the Q^T,
+// dO^T and dQ^T registers alone take 256 of the wave's 512.
+template <int D>
+constexpr int dq_keys() { return D == 256 ? 32 : 64; }
 constexpr int kDkvKeys = 16 * kBwdWaves;   // keys per dK/dV workgroup (16 per wave)
 constexpr int kDkvRows = 32;               // query rows per Q/dO tile in the dK/dV kernel
 
@@ -165,7 +168,7 @@ template <int D, bool CAUSAL>
 __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, lds_char* kb0, lds_char* kb1,
                                             lds_char* vb0, lds_char* vb1) {
   using S = BwdShape<D>;
-  constexpr int BN = kDqKeys, BM = kDqRows;
+  constexpr int BN = dq_keys<D>(), BM = kDqRows;
   constexpr int KB = BN / 32, KC = BN / 16;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -482,9 +485,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* qt0,
 }  // namespace
 }  // namespace fa
 
-#define FA_BWD_DQ(D, CAUSAL, NAME)                                                         \
-  extern "C" __global__ void __launch_bounds__(64 * fa::kBwdWaves, 2) NAME(fa::BwdParams p) { \
-    constexpr int T = fa::kDqKeys * 2 * D;                                                 \
+#define FA_BWD_DQ(D, CAUSAL, NAME, WPE)                                                    \
+  extern "C" __global__ void __launch_bounds__(64 * fa::kBwdWaves, WPE) NAME(fa::BwdParams p) { \
+    constexpr int T = fa::dq_keys<D>() * 2 * D;                                            \
     __shared__ __attribute__((aligned(1024))) char k0[T];                                  \
     __shared__ __attribute__((aligned(1024))) char k1[T];                                  \
     __shared__ __attribute__((aligned(1024))) char v0[T];                                  \
@@ -493,8 +496,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* qt0,
                                (fa::lds_char*)v1);                                         \
   }
 
-#define FA_BWD_DKDV(D, CAUSAL, NAME)                                                       \
-  extern "C" __global__ void __launch_bounds__(64 * fa::kDkvWaves, 3) NAME(fa::BwdParams p) { \
+#define FA_BWD_DKDV(D, CAUSAL, NAME, WPE)                                                  \
+  extern "C" __global__ void __launch_bounds__(64 * fa::kDkvWaves, WPE) NAME(fa::BwdParams p) { \
     using St = fa::DkvStage<D>;                                                            \
     __shared__ __attribute__((aligned(1024))) char q0[St::TILE];                           \
     __shared__ __attribute__((aligned(1024))) char q1[St::TILE];                           \
@@ -507,22 +510,26 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* qt0,
                                  (fa::lds_char*)s0, (fa::lds_char*)s1);                    \
   }
 
-FA_BWD_DQ(32, false, fa_bwd_dq_d32_nomask)
-FA_BWD_DQ(32, true, fa_bwd_dq_d32_causal)
-FA_BWD_DQ(64, false, fa_bwd_dq_d64_nomask)
-FA_BWD_DQ(64, true, fa_bwd_dq_d64_causal)
-FA_BWD_DQ(128, false, fa_bwd_dq_d128_nomask)
-FA_BWD_DQ(128, true, fa_bwd_dq_d128_causal)
-FA_BWD_DKDV(32, false, fa_bwd_dkdv_d32_nomask)
-FA_BWD_DKDV(32, true, fa_bwd_dkdv_d32_causal)
-FA_BWD_DKDV(64, false, fa_bwd_dkdv_d64_nomask)
-FA_BWD_DKDV(64, true, fa_bwd_dkdv_d64_causal)
-FA_BWD_DKDV(128, false, fa_bwd_dkdv_d128_nomask)
-FA_BWD_DKDV(128, true, fa_bwd_dkdv_d128_causal)
+FA_BWD_DQ(32, false, fa_bwd_dq_d32_nomask, 2)
+FA_BWD_DQ(32, true, fa_bwd_dq_d32_causal, 2)
+FA_BWD_DQ(64, false, fa_bwd_dq_d64_nomask, 2)
+FA_BWD_DQ(64, true, fa_bwd_dq_d64_causal, 2)
+FA_BWD_DQ(128, false, fa_bwd_dq_d128_nomask, 2)
+FA_BWD_DQ(128, true, fa_bwd_dq_d128_causal, 2)
+FA_BWD_DQ(256, false, fa_bwd_dq_d256_nomask, 1)
+FA_BWD_DQ(256, true, fa_bwd_dq_d256_causal, 1)
+FA_BWD_DKDV(32, false, fa_bwd_dkdv_d32_nomask, 3)
+FA_BWD_DKDV(32, true, fa_bwd_dkdv_d32_causal, 3)
+FA_BWD_DKDV(64, false, fa_bwd_dkdv_d64_nomask, 3)
+FA_BWD_DKDV(64, true, fa_bwd_dkdv_d64_causal, 3)
+FA_BWD_DKDV(128, false, fa_bwd_dkdv_d128_nomask, 3)
+FA_BWD_DKDV(128, true, fa_bwd_dkdv_d128_causal, 3)
+FA_BWD_DKDV(256, false, fa_bwd_dkdv_d256_nomask, 1)
+FA_BWD_DKDV(256, true, fa_bwd_dkdv_d256_causal, 1)
 
 namespace fa {
 
-bool bwd_supported_d(int d) { return d == 32 || d == 64 || d == 128; }
+bool bwd_supported_d(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
 
 int bwd_dq_grid_blocks(int B, int Hq, int Nq) { return ((Nq + kDqRows - 1) / kDqRows) * B * Hq; }
 int bwd_dkdv_grid_blocks(int B, int Hkv, int Nk) {
@@ -530,15 +537,17 @@ int bwd_dkdv_grid_blocks(int B, int Hkv, int Nk) {
 }
 
 const char* bwd_kernel_name(int d, bool causal, int stage) {
-  static const char* const names[2][3][2] = {
+  static const char* const names[2][4][2] = {
       {{"fa_bwd_dq_d32_nomask", "fa_bwd_dq_d32_causal"},
        {"fa_bwd_dq_d64_nomask", "fa_bwd_dq_d64_causal"},
-       {"fa_bwd_dq_d128_nomask", "fa_bwd_dq_d128_causal"}},
+       {"fa_bwd_dq_d128_nomask", "fa_bwd_dq_d128_causal"},
+       {"fa_bwd_dq_d256_nomask", "fa_bwd_dq_d256_causal"}},
       {{"fa_bwd_dkdv_d32_nomask", "fa_bwd_dkdv_d32_causal"},
        {"fa_bwd_dkdv_d64_nomask", "fa_bwd_dkdv_d64_causal"},
-       {"fa_bwd_dkdv_d128_nomask", "fa_bwd_dkdv_d128_causal"}}};
+       {"fa_bwd_dkdv_d128_nomask", "fa_bwd_dkdv_d128_causal"},
+       {"fa_bwd_dkdv_d256_nomask", "fa_bwd_dkdv_d256_causal"}}};
   if (stage != 0 && stage != 1) return nullptr;
-  const int di = d == 32 ? 0 : d == 64 ? 1 : d == 128 ? 2 : -1;
+  const int di = d == 32 ? 0 : d == 64 ? 1 : d == 128 ? 2 : d == 256 ? 3 : -1;
   if (di < 0) return nullptr;
   return names[stage][di][causal ? 1 : 0];
 }
@@ -555,6 +564,7 @@ hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s) {
     FA_PICK(32)
     FA_PICK(64)
     FA_PICK(128)
+    FA_PICK(256)
     default: return hipErrorInvalidValue;
   }
 #undef FA_PICK

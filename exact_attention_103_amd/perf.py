@@ -4,7 +4,8 @@
 
 Prints one JSON line per workload: the kernel that ran, the median launch
 time (HIP events on the launch stream) and TFLOP/s for the forward (flop =
-4*B*H*Nq*Nk*d, halved when causal) or GB/s for the decode (K + V cache read
+4*B*H*Nq*Nk*d, halved when causal), for the backward (the algorithmic five
+products, 2.5x the forward's flop) or GB/s for the decode (K + V cache read
 once, plus q, O and LSE; for the serving decode only each sequence's first
 seqlens[b] keys count; for the fp8 quantisation 3 bytes per element).  Inputs are random bf16 tensors of the workload's
 shape and scaling; the forward's speed does not depend on the values.
@@ -78,6 +79,23 @@ def main():
                           "tflops": round(flop / ms / 1e9, 1),
                           "pct_of_2500": round(100 * flop / ms / 1e9 / 2500, 1)}), flush=True)
         del q, k, v, o, lse
+    for name, B, H, N, d, causal, sc in FWD:
+        q = (torch.randn(B, H, N, d, device="cuda") * sc).to(torch.bfloat16)
+        k = (torch.randn(B, H, N, d, device="cuda") * sc).to(torch.bfloat16)
+        v = torch.randn(B, H, N, d, device="cuda").to(torch.bfloat16)
+        do = torch.randn(B, H, N, d, device="cuda").to(torch.bfloat16)
+        o, lse = fa.fwd(q, k, v, causal=causal)
+        ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N), dtype=torch.uint8, device="cuda")
+        ms = _time(lambda: fa.bwd(q, k, v, o, lse, do, causal=causal, workspace=ws),
+                   args.iters, args.warmup)
+        flop = 2.5 * 4.0 * B * H * N * N * d / (2 if causal else 1)
+        print(json.dumps({"workload": name + "_bwd", "B": B, "H": H, "N": N, "d": d,
+                          "causal": causal,
+                          "kernels": [fa.fa_bwd_kernel_name(d, int(causal), 0),
+                                      fa.fa_bwd_kernel_name(d, int(causal), 1)],
+                          "ms": round(ms, 4), "tflops": round(flop / ms / 1e9, 1),
+                          "pct_of_2500": round(100 * flop / ms / 1e9 / 2500, 1)}), flush=True)
+        del q, k, v, do, o, lse, ws
     for name, B, H, N, d, causal, sc in FWD:
         if d not in (64, 128):
             continue

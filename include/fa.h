@@ -44,8 +44,8 @@ enum fa_status {
   FA_ERR_NULL = -1,       /* a required pointer is NULL                      */
   FA_ERR_SHAPE = -2,      /* B, H or N <= 0, Hq % Hkv != 0, causal && Nq > Nk,
                              serving decode Nq outside 1..16                 */
-  FA_ERR_HEAD_DIM = -3,   /* d not in {32, 64, 128, 256} ({32, 64, 128} bwd,
-                             {64, 128} fp8 forward)                           */
+  FA_ERR_HEAD_DIM = -3,   /* d not in {32, 64, 128, 256} ({64, 128} fp8
+                             forward)                                         */
   FA_ERR_ALIGN = -4,      /* a tensor pointer is not 16-byte aligned         */
   FA_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required         */
   FA_ERR_SPLITS = -6,     /* num_splits outside 0 .. fa_decode_max_splits()  */
@@ -298,7 +298,7 @@ int fa_decode_max_splits(int Nk);
  *   lse        fp32 [B][Hq][Nq]        fa_fwd's LSE (natural log)
  *   dq         bf16 [B][Hq][Nq][d]     output
  *   dk, dv     bf16 [B][Hkv][Nk][d]    outputs
- *   d          32, 64 or 128
+ *   d          32, 64, 128 or 256
  *   scale, causal  the values the forward used
  *   workspace  device scratch of at least fa_bwd_workspace_size(B, Hq, Nq)
  *              bytes (Delta, fp32), 16-byte aligned, owned by the caller; it

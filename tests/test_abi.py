@@ -93,12 +93,12 @@ def test_kernel_names():
 
 
 def test_bwd_kernel_names_and_workspace():
-    for d in (32, 64, 128):
+    for d in (32, 64, 128, 256):
         assert fa.fa_bwd_kernel_name(d, 0, 0) == f"fa_bwd_dq_d{d}_nomask"
         assert fa.fa_bwd_kernel_name(d, 1, 0) == f"fa_bwd_dq_d{d}_causal"
         assert fa.fa_bwd_kernel_name(d, 0, 1) == f"fa_bwd_dkdv_d{d}_nomask"
         assert fa.fa_bwd_kernel_name(d, 1, 1) == f"fa_bwd_dkdv_d{d}_causal"
-    assert fa.fa_bwd_kernel_name(256, 0, 0) is None
+    assert fa.fa_bwd_kernel_name(96, 0, 0) is None
     assert fa.fa_bwd_kernel_name(128, 0, 2) is None
     assert fa.fa_bwd_kernel_name(128, 2, 0) is None
     assert fa.fa_bwd_workspace_size(2, 4, 100) == 4 * 2 * 4 * 100
@@ -292,7 +292,7 @@ def _bwd(**kw):
     (dict(lse=0), -1), (dict(dq=0), -1), (dict(dk=0), -1), (dict(dv=0), -1),
     (dict(B=0), -2), (dict(Hq=3), -2), (dict(Nq=0), -2), (dict(causal=2), -2),
     (dict(Nq=65, Nk=64), -2),
-    (dict(d=256), -3), (dict(d=48), -3),
+    (dict(d=96), -3), (dict(d=48), -3),
     (dict(scale=0.0), -8), (dict(scale=math.inf), -8),
     (dict(ws=0), -5), (dict(ws_bytes=4 * 4 * 64 - 1), -5),
     (dict(q=BQ + 8), -4), (dict(dk=BDK + 2), -4), (dict(ws=BW + 4), -4),

@@ -53,6 +53,9 @@ ODD = [
     (1, 8, 8, 129, 129, 128, True),
     (1, 8, 1, 150, 150, 64, False),   # eight query heads per KV head
     (2, 16, 2, 97, 161, 128, True),   # GQA 8, Nq < Nk, ragged in both
+    (1, 2, 1, 100, 100, 256, True),   # d = 256: 32-key dQ tiles, one wave per SIMD
+    (1, 4, 2, 77, 210, 256, True),
+    (1, 2, 2, 130, 97, 256, False),
 ]
 
 
@@ -121,6 +124,10 @@ def test_bwd_sweep_d64_sampled():
     _workload_case("sweep_d64", [(1, 9)])
 
 
+def test_bwd_sweep_d256_sampled():
+    _workload_case("sweep_d256", [(0, 2)], rows_per_head=512, keys_per_head=512)
+
+
 def test_bwd_long_causal_sampled():
     # 256 seeded query rows (dQ) and 256 seeded keys (dK, dV) of one head.
     _workload_case("long", [(0, 5)], rows_per_head=256, keys_per_head=256)
@@ -143,7 +150,7 @@ def test_bwd_deterministic():
 def test_bwd_rejects_unsupported():
     import torch
     announce("bwd error paths")
-    q = torch.zeros(1, 2, 64, 256, dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros(1, 2, 64, 96, dtype=torch.bfloat16, device="cuda")
     lse = torch.zeros(1, 2, 64, dtype=torch.float32, device="cuda")
     with pytest.raises(fa.FAError) as e:
         fa.bwd(q, q.clone(), q.clone(), q.clone(), lse, q.clone())

@@ -146,6 +146,7 @@ BWD = [  # (B, Hq, Hkv, Nq, Nk, d, causal)
     (1, 2, 2, 700, 1000, 64, False),
     (1, 4, 2, 1000, 1000, 128, True),
     (1, 2, 1, 333, 1111, 128, False),
+    (1, 4, 2, 700, 1000, 256, True),
 ]
 
 
