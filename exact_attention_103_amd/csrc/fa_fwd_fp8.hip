@@ -64,9 +64,27 @@ struct F8Shape {
   static_assert(D % 64 == 0, "fp8 head dim");
 };
 
-// LDS tiles: 16-byte chunk c of row r at c ^ ((r / 2) mod CPR).
+// LDS tiles: 16-byte chunk c of row r at c ^ X(r).  Two read patterns meet
+// there:
+//  * the K operand (16-byte reads, 16 lanes per LDS pass): 16 consecutive
+//    rows, one chunk each, so X must separate rows sharing a bank-line
+//    position (a bijection on the row's line index);
+//  * the V^T operand (8-bit transposing 8-byte reads, 32 lanes per pass):
+//    rows {0..3, 8..11} + 4h, chunks 2db and 2db + 1, so the rows of one
+//    line position must differ in X's bit 1.
+// 128-byte rows (two per line): X = i with its two low bits swapped,
+// i = (r / 2) mod 8; 64-byte rows (four per line): X = (r / 4) mod 4.  Both
+// touch every bank once per pass in either pattern (an earlier X = i put two
+// lanes on each bank of the V^T reads).
 template <int RB>
-__device__ __forceinline__ int f8_xor(int r) { return (r >> 1) & (RB / 16 - 1); }
+__device__ __forceinline__ int f8_xor(int r) {
+  if constexpr (RB >= 128) {
+    const int i = (r >> 1) & 7;
+    return ((i & 1) << 1) | ((i >> 1) & 1) | (i & 4);
+  } else {
+    return (r >> 2) & 3;
+  }
+}
 
 __device__ __forceinline__ float f8_half_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
