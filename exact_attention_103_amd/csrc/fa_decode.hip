@@ -232,18 +232,21 @@ __device__ __forceinline__ void decode_split_body(const DecodeParams& p, lds_cha
   }
 
   // Merge the four waves' states through LDS: lane (grp, col) owns O^T rows
-  // 16db + 4grp + r of query col.
+  // 16db + 4grp + r of query col.  The accumulator rows are padded by 4
+  // floats, so the 16 columns of one 16-byte write land 4 banks apart (with
+  // rows of exactly D floats they all hit the same 4 banks).
   const float lt = group4_sum(l);
+  constexpr int AR = D + 4;                      // floats per accumulator row
   float* sm_m = mlds;                            // [4][16]
   float* sm_l = sm_m + kDecWaves * 16;           // [4][16]
-  float* sm_acc = sm_l + kDecWaves * 16;         // [4][16][D]
+  float* sm_acc = sm_l + kDecWaves * 16;         // [4][16][AR]
   if (grp == 0) {
     sm_m[wave * 16 + col] = m;
     sm_l[wave * 16 + col] = lt;
   }
 #pragma unroll
   for (int db = 0; db < S::NDB; ++db)
-    *reinterpret_cast<float4*>(sm_acc + ((size_t)wave * 16 + col) * D + 16 * db + 4 * grp) =
+    *reinterpret_cast<float4*>(sm_acc + ((size_t)wave * 16 + col) * AR + 16 * db + 4 * grp) =
         make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
   __syncthreads();
 
@@ -259,7 +262,7 @@ __device__ __forceinline__ void decode_split_body(const DecodeParams& p, lds_cha
     for (int w = 0; w < kDecWaves; ++w) {
       const float wt = __builtin_amdgcn_exp2f(sm_m[w * 16 + gq] - M);
       W += wt * sm_l[w * 16 + gq];
-      O += wt * sm_acc[((size_t)w * 16 + gq) * D + dd];
+      O += wt * sm_acc[((size_t)w * 16 + gq) * AR + dd];
     }
     const size_t ps = ((size_t)(b * p.Hq + h0 + gh) * nq + gr) * p.splits + s;
     if (W > 0.f) {
@@ -349,7 +352,7 @@ __device__ __forceinline__ void decode_merge_body(const DecodeParams& p) {
   extern "C" __global__ void __launch_bounds__(fa::kDecThreads, 2) NAME(fa::DecodeParams p) { \
     __shared__ __attribute__((aligned(1024))) char vs0[fa::kDecWaves * fa::DecShape<D>::VTILE]; \
     __shared__ __attribute__((aligned(1024))) char vs1[fa::kDecWaves * fa::DecShape<D>::VTILE]; \
-    __shared__ __attribute__((aligned(16))) float mlds[fa::kDecWaves * 16 * (2 + D)];   \
+    __shared__ __attribute__((aligned(16))) float mlds[fa::kDecWaves * 16 * (2 + D + 4)]; \
     fa::decode_split_body<D, GT, SERVE>(p, (fa::lds_char*)vs0, (fa::lds_char*)vs1, mlds); \
   }
 #define FA_DEC_SPLIT(D, GT)                                          \
