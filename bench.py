@@ -363,6 +363,12 @@ def workload_legs(fa, stream, steps, names=("train_nc", "train_c", "sweep_d32", 
     return out
 
 
+def _under_profiler():
+    """True inside a rocprofv3 run (its tool library is preloaded)."""
+    pre = os.environ.get("LD_PRELOAD", "")
+    return "rocprof" in pre or any(k.startswith("ROCPROF") for k in os.environ)
+
+
 def sample_sclk(call, seconds=1.0):
     """Shader clock (MHz) samples from amd-smi while `call` runs back to back
     for about `seconds`.  Returns the samples' median/min/max, or a note with
@@ -543,7 +549,12 @@ def main():
         },
         "cpu_baseline": None,
     }
-    if not args.no_sclk:
+    if not args.no_sclk and _under_profiler():
+        # amd-smi would start inside the profiler's preloaded library and
+        # replace itself with its interpreter after that library touched the
+        # GPU; profiled runs take no clock samples.
+        out["sclk"] = {"mhz_median": None, "note": "skipped under a profiler"}
+    elif not args.no_sclk:
         def fwd_only():
             fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                       fcfg.B, fcfg.Hq, fcfg.Hkv, fcfg.Nq, fcfg.Nk, fcfg.d, fcfg.scale,
