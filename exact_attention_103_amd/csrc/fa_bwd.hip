@@ -100,26 +100,55 @@ constexpr int dq_keys() { return D == 256 ? 32 : 64; }
 constexpr int kDkvKeys = 16 * kBwdWaves;   // keys per dK/dV workgroup (16 per wave)
 constexpr int kDkvRows = 32;               // query rows per Q/dO tile in the dK/dV kernel
 
-// Direct global -> LDS copy of ROWS rows (from row r0, rows past nrows re-read
-// row nrows-1) of a row-major [.][D] bf16 matrix, swizzled with bwd_xor.
-// Wave load i writes 1 KB block i*NW + wave of the tile; lane l of it fetches
-// the global chunk whose swizzled position is that block's l-th chunk.
-template <int D, int ROWS, int SW = 0, int NW = kBwdWaves>
-__device__ __forceinline__ void dma_rows(const uint16_t* base, int r0, int nrows, lds_char* tile,
-                                         int wave, int lane) {
-  constexpr int CPR = D / 8;
-  constexpr int BLKS = ROWS * CPR / 64;
-  constexpr int LOADS = (BLKS + NW - 1) / NW;
+// Direct global -> LDS copy of a ROWS-row tile of a row-major [.][D] bf16
+// matrix, swizzled with bwd_xor.  Wave load i writes 1 KB block i*NW + wave
+// of the tile; lane l of it fetches the global chunk whose swizzled position
+// is that block's l-th chunk.  The per-lane byte offsets within a tile do
+// not depend on which tile is copied, so they are computed once
+// (dma_offsets); a copy is then one buffer load per block, through a buffer
+// resource whose size ends at the matrix's last row: rows past it read as
+// zero, which the kernels mask (probability 0) like any other row past the
+// end.
+template <int D, int ROWS, int NW>
+struct Dma {
+  static constexpr int CPR = D / 8;
+  static constexpr int BLKS = ROWS * CPR / 64;
+  static constexpr int LOADS = (BLKS + NW - 1) / NW;
   static_assert((ROWS * CPR) % 64 == 0, "whole 1 KB blocks");
+};
+
+template <int D, int ROWS, int SW = 0, int NW = kBwdWaves>
+__device__ __forceinline__ void dma_offsets(int wave, int lane, int* off) {
+  using T = Dma<D, ROWS, NW>;
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
+  for (int i = 0; i < T::LOADS; ++i) {
+    const int P = (i * NW + wave) * 64 + lane;
+    const int row = P / T::CPR;
+    const int c = (P % T::CPR) ^ bwd_xor<2 * D, SW>(row);
+    off[i] = row * 2 * D + c * 16;
+  }
+}
+
+// Buffer resource over rows r0 .. r0 + ROWS - 1 of a row-major [.][D] bf16
+// matrix of `nrows` rows (rows at or past nrows read as zero).
+template <int D, int ROWS>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int r0,
+                                                            int nrows) {
+  const int rows = max(0, min(nrows - r0, ROWS));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + (size_t)r0 * D), 0,
+                                           rows * D * 2, 0x00020000);
+}
+
+template <int D, int ROWS, int NW = kBwdWaves>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, const int* off,
+                                         lds_char* tile, int wave) {
+  using T = Dma<D, ROWS, NW>;
+#pragma unroll
+  for (int i = 0; i < T::LOADS; ++i) {
     const int blk = i * NW + wave;   // uniform across the wave
-    if (BLKS % NW != 0 && blk >= BLKS) break;
-    const int P = blk * 64 + lane;
-    const int row = P / CPR;
-    const int c = (P % CPR) ^ bwd_xor<2 * D, SW>(row);
-    const int r = min(r0 + row, nrows - 1);
-    __builtin_amdgcn_global_load_lds(base + (size_t)r * D + c * 8, tile + blk * 1024, 16, 0, 0);
+    if (T::BLKS % NW != 0 && blk >= T::BLKS) break;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(tile + blk * 1024), 16, off[i], 0, 0, 0);
   }
 }
 
@@ -221,6 +250,8 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, lds_char* kb0, l
   const int koff = n * S::RB;
   int toff[2][S::DB];
   tr_offsets<D>(lane, toff);
+  int doff[Dma<D, BN, kBwdWaves>::LOADS];
+  dma_offsets<D, BN>(wave, lane, doff);
 
   f32x16 dq[S::DB];
 #pragma unroll
@@ -242,8 +273,8 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, lds_char* kb0, l
     const int j0 = j * BN;
     FA_STAGE_FENCE();
     if (j + 1 < nkt) {
-      dma_rows<D, BN>(kbase, j0 + BN, p.Nk, kw, wave, lane);
-      dma_rows<D, BN>(vbase, j0 + BN, p.Nk, vw, wave, lane);
+      dma_tile<D, BN>(rows_rsrc<D, BN>(kbase, j0 + BN, p.Nk), doff, kw, wave);
+      dma_tile<D, BN>(rows_rsrc<D, BN>(vbase, j0 + BN, p.Nk), doff, vw, wave);
     }
     FA_STAGE_FENCE();
     f32x16 sacc[KB], dpacc[KB];
@@ -278,8 +309,8 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, lds_char* kb0, l
     __syncthreads();
   };
 
-  dma_rows<D, BN>(kbase, 0, p.Nk, kb0, wave, lane);
-  dma_rows<D, BN>(vbase, 0, p.Nk, vb0, wave, lane);
+  dma_tile<D, BN>(rows_rsrc<D, BN>(kbase, 0, p.Nk), doff, kb0, wave);
+  dma_tile<D, BN>(rows_rsrc<D, BN>(vbase, 0, p.Nk), doff, vb0, wave);
   __syncthreads();
   for (int j = 0; j < nkt; j += 2) {
     step(kb0, vb0, kb1, vb1, j);
@@ -382,25 +413,36 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* qt0,
     dv[db] = f32x4{};
   }
 
-  auto tile_row = [&](int s) { return qstart + (s % nqt) * BM; };
-  auto load = [&](int s, lds_char* qt, lds_char* dt, lds_char* st) {
-    const int h = g * p.group + s / nqt, i0 = tile_row(s);
-    const size_t hb = (size_t)(b * p.Hq + h) * p.Nq;
-    dma_rows<D, BM, 1, NW>(p.q + hb * D, i0, p.Nq, qt, wave, lane);
-    dma_rows<D, BM, 1, NW>(p.dout + hb * D, i0, p.Nq, dt, wave, lane);
+  int doff[Dma<D, BM, NW>::LOADS];
+  dma_offsets<D, BM, 1, NW>(wave, lane, doff);
+  // Steps walk the query heads of the group, each over its row tiles
+  // qstart, qstart + BM, ...: the tile to load next and the tile of the
+  // current step advance by one each time (no division per step).
+  int ld_h = g * p.group, ld_i0 = qstart;
+  auto load = [&](lds_char* qt, lds_char* dt, lds_char* st) {
+    const size_t hb = (size_t)(b * p.Hq + ld_h) * p.Nq;
+    dma_tile<D, BM, NW>(rows_rsrc<D, BM>(p.q + hb * D, ld_i0, p.Nq), doff, qt, wave);
+    dma_tile<D, BM, NW>(rows_rsrc<D, BM>(p.dout + hb * D, ld_i0, p.Nq), doff, dt, wave);
     if (wave == 0) {   // lanes 0-31: LSE of the BM rows, lanes 32-63: Delta
       const float* src = (lane < BM ? p.lse : p.delta - BM) + hb;
-      __builtin_amdgcn_global_load_lds(src + min(i0 + (lane & (BM - 1)), p.Nq - 1) + (lane & BM),
+      __builtin_amdgcn_global_load_lds(src + min(ld_i0 + (lane & (BM - 1)), p.Nq - 1) + (lane & BM),
                                        st, 4, 0, 0);
     }
+    ld_i0 += BM;
+    if (ld_i0 >= p.Nq) {
+      ld_i0 = qstart;
+      ++ld_h;
+    }
   };
+  int cur_i0 = qstart;
 
   auto step = [&](const lds_char* qt, const lds_char* dt, const lds_char* st, lds_char* qw,
                   lds_char* dw, lds_char* sw, int s) {
     FA_STAGE_FENCE();
-    if (s + 1 < steps) load(s + 1, qw, dw, sw);
+    if (s + 1 < steps) load(qw, dw, sw);
     FA_STAGE_FENCE();
-    const int i0 = tile_row(s);
+    const int i0 = cur_i0;
+    cur_i0 = cur_i0 + BM >= p.Nq ? qstart : cur_i0 + BM;
     const __attribute__((address_space(3))) f32x4* lse4 =
         (const __attribute__((address_space(3))) f32x4*)st;
     const __attribute__((address_space(3))) f32x4* del4 = lse4 + BM / 4;
@@ -455,7 +497,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* qt0,
     __syncthreads();
   };
 
-  load(0, qt0, dt0, st0);
+  load(qt0, dt0, st0);
   __syncthreads();
   for (int s = 0; s < steps; s += 2) {
     step(qt0, dt0, st0, qt1, dt1, st1, s);
