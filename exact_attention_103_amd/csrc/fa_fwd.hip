@@ -34,11 +34,11 @@
 // Normalisation by 1/l happens once at the end ([Evolution] §2 and §3), and
 // only O (bf16) and LSE (fp32) are written.
 //
-// K/V tiles travel HBM -> LDS with direct-to-LDS loads (global_load_lds,
-// no register staging) into two LDS stages: tile j+1 is in flight while tile
-// j is computed (the CDNA counterpart of the asynchronous copies of
-// [Evolution] §4).  Both tiles use XOR swizzles on 16-byte chunks chosen so
-// that the MFMA operand reads spread over all LDS banks.
+// K/V tiles travel HBM -> LDS with direct-to-LDS buffer loads (no register
+// staging) into two LDS stages: tile j+1 is in flight while tile j is
+// computed (the CDNA counterpart of the asynchronous copies of [Evolution]
+// §4).  The K tile has padded rows and the V tile an XOR swizzle on 16-byte
+// chunks, chosen so that the MFMA operand reads spread over all LDS banks.
 
 #include "fa_internal.h"
 
