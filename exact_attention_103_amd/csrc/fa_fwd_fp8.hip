@@ -26,6 +26,13 @@
 // product), so K and Q use contiguous d ranges, and V^T is read with the key
 // order that the P^T registers hold.  O = v_factor * acc / l (bf16), LSE in
 // natural log of the scaled scores.
+//
+// Schedule: eight waves of 32 query rows per workgroup, one 64-key tile per
+// step.  The P V product of a tile runs one step after its probabilities,
+// and the two waves that share a SIMD issue each step's MFMAs and its
+// exponentials in opposite orders, so one wave's softmax overlaps the other
+// wave's products.  K and V tiles are copied two steps ahead into three LDS
+// buffers each, so the per-step barrier rarely waits for memory.
 
 #include "fa_internal.h"
 
@@ -95,19 +102,51 @@ __device__ __forceinline__ float f8_half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Raw buffer resource over the `rows` keys of one tile at `base` (fp8
+// [key][D]): loads past those rows return zero without touching memory,
+// which covers the key tail and the tiles past the end (rows = 0).
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t f8_tile_rsrc(const uint8_t* base, int rows) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, rows * D, 0x00020000);
+}
+// A tile is copied with direct buffer -> LDS loads: wave w writes the 1 KB
+// blocks i*NW + w, lane l the l-th 16-byte chunk of the block, which holds
+// row P / CPR, swizzled chunk P % CPR of the tile (P = 64 * block + l).  The
+// per-lane global offsets are fixed for the kernel, so the loads' only
+// vector operand is never rewritten while a copy is in flight.
 template <int D, int NW>
-__device__ __forceinline__ void f8_load_tile(const uint8_t* base, int j0, int Nk, lds_char* tile,
-                                             int wave, int lane) {
+__device__ __forceinline__ void f8_load_offsets(int wave, int lane, int* voff) {
+  using S = F8Shape<D, NW>;
+#pragma unroll
+  for (int i = 0; i < S::LOADS; ++i) {
+    const int P = (i * NW + wave) * 64 + lane;
+    const int row = P / S::CPR;
+    voff[i] = row * D + (((P % S::CPR) ^ f8_xor<S::RB>(row)) << 4);
+  }
+}
+template <int D, int NW>
+__device__ __forceinline__ void f8_load_tile(__amdgpu_buffer_rsrc_t rs, lds_char* tile, int wave,
+                                             const int* voff) {
   using S = F8Shape<D, NW>;
 #pragma unroll
   for (int i = 0; i < S::LOADS; ++i) {
     const int blk = i * NW + wave;
     if (S::BLKS % NW != 0 && blk >= S::BLKS) break;
-    const int P = blk * 64 + lane;
-    const int row = P / S::CPR;
-    const int c = (P % S::CPR) ^ f8_xor<S::RB>(row);
-    const int key = min(j0 + row, Nk - 1);
-    __builtin_amdgcn_global_load_lds(base + (size_t)key * D + c * 16, tile + blk * 1024, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(tile + blk * 1024), 16, voff[i], 0, 0, 0);
+  }
+}
+
+// Compile-time loop (every unrolled step's LDS buffers are then constants).
+template <int I>
+struct F8Int {
+  static constexpr int value = I;
+};
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(F8Int<I>{});
+    static_for<I + 1, N>(f);
   }
 }
 
@@ -117,7 +156,8 @@ __device__ __forceinline__ v8i f8_mfma_operand(v4i lo, v4i hi) {
 
 template <int D, int NW, bool CAUSAL>
 __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0, lds_char* kb1,
-                                             lds_char* vb0, lds_char* vb1) {
+                                             lds_char* kb2, lds_char* vb0, lds_char* vb1,
+                                             lds_char* vb2) {
   using S = F8Shape<D, NW>;
   constexpr int BN = S::BN;
   const int tid = threadIdx.x;
@@ -240,32 +280,65 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
     return f8_half_max(x) * cexp;
   };
 
-  v8i pf = v8i{};   // fp8 P^T of the current tile (B operand of the PV products)
-  auto step = [&](const lds_char* kr, const lds_char* vr, lds_char* kw, lds_char* vw,
-                  f32x16 (&sc)[S::KB], f32x16 (&sn)[S::KB], int j) {
-    const int j0 = j * BN;
+  // P V of a tile: O^T += V^T P^T, the V^T operand from 8-bit transposing
+  // reads of the tile's V buffer.
+  auto pv = [&](const lds_char* vt, const v8i& pft) {
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db) {
+      v8i a;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i*)(vt + voff[db] + 16 * u * S::RB));
+        a[2 * u] = t[0];
+        a[2 * u + 1] = t[1];
+      }
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pft, oacc[db], 0, 0, 0, 127, 0, 127);
+    }
+  };
+
+  int ldoff[S::LOADS];
+  f8_load_offsets<D, NW>(wave, lane, ldoff);
+  auto load = [&](const uint8_t* base, int t, lds_char* tile) {
+    const int rows = t < nkt ? min(p.Nk - t * BN, BN) : 0;
+    f8_load_tile<D, NW>(f8_tile_rsrc<D>(base + (size_t)t * BN * D, rows), tile, wave, ldoff);
+  };
+
+  // One step for tile j.  The P V product of a tile runs one step after its
+  // probabilities: step j issues S^T of tile j+1 and P V of tile j-1 on the
+  // MFMA pipe, and neither depends on the VALU work that turns tile j's
+  // scores into fp8 probabilities.  The two waves that share a SIMD (waves w
+  // and w+4 of the workgroup) take the two halves in opposite orders (wave
+  // group G = 1: products, then probabilities; G = 0: probabilities, then
+  // products), so that one wave's exponentials run while the other wave's
+  // MFMAs do.  A scheduling barrier keeps each order as written.
+  //
+  // Buffers: K_{j+1} and V_{j-1} are read here; K_{j+3} is loaded over K_j
+  // (read in the previous step) and V_{j+1} over V_{j-2}.  Every copy is
+  // thus issued two steps before its tile is read, and the step ends with a
+  // workgroup barrier that waits only for the previous step's copies (the
+  // two issued here may stay in flight).  The loads are unconditional
+  // (tiles past the end read zero rows), which keeps that count exact.
+  //
+  // On entry sc holds S^T of tile j and pf the fp8 probabilities of tile
+  // j-1 (unused when j = 0).
+  v8i pf = v8i{};
+  auto step = [&](const lds_char* kr, const lds_char* vprev, lds_char* kw, lds_char* vw,
+                  f32x16 (&sc)[S::KB], f32x16 (&sn)[S::KB], int j, auto group) {
     if (needs_mask(j)) mask_tile(sc, j);
     FA_STAGE_FENCE();
-    if (j + 2 < nkt) f8_load_tile<D, NW>(kbase, j0 + 2 * BN, p.Nk, kw, wave, lane);
-    if (j + 1 < nkt) f8_load_tile<D, NW>(vbase, j0 + BN, p.Nk, vw, wave, lane);
+    load(kbase, j + 3, kw);
+    load(vbase, j + 1, vw);
     FA_STAGE_FENCE();
 
-    // S^T of tile j+1 on the MFMA pipe next to tile j's softmax.
-    s_tile(kr, sn);
-
-    // At d = 128, LLVM's instruction group strategy 0 (LDS reads interleaved
-    // with the MFMAs) schedules this section: +2.3% at the long causal
-    // prefill, +2.6% at B=8 H=16 N=2048 non-causal, +5.3% at B=2 H=16 N=4096
-    // causal.  At d = 64 it measured about -4%.
-    if constexpr (D == 128) __builtin_amdgcn_iglp_opt(0);
     // P^T = 2^(S*c - m) rounded to fp8: dword w holds keys of block w/4,
-    // registers 4(w%4) .. +3, which the V^T reads below follow.  The second
-    // pass runs only after the reference moved (see kF8SumLimit).  The two
+    // registers 4(w%4) .. +3, which the V^T reads follow.  The two
     // conversions of dword w overwrite both of its halves; passing the
     // previous tile's dword as the "old" operand keeps the same registers
-    // and saves zeroing them every tile.
+    // and saves zeroing them.
+    v8i pn = pf;
     float t0, t1;
-    for (int pass = 0;; ++pass) {
+    auto probs = [&]() {
       const float nm = -m_run;
       t0 = 0.f;
       t1 = 0.f;
@@ -278,17 +351,33 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
         const float e3 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 3], cexp, nm));
         t0 += e0 + e2;
         t1 += e1 + e3;
-        int x = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, pf[w], false);
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, pn[w], false);
         x = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, x, true);
-        pf[w] = x;
+        pn[w] = x;
       }
-      // The bit-pattern test on the next tile's scores (a NaN) is never true
-      // for finite inputs; reading them here keeps their MFMAs ahead of the
-      // branch, next to this tile's exponentials.
-      bool bad = !(t0 + t1 < kF8SumLimit);
+    };
+    auto products = [&]() {
+      s_tile(kr, sn);
+      if (j > 0) pv(vprev, pf);
+    };
+    if constexpr (decltype(group)::value) {
+      products();
+      __builtin_amdgcn_sched_barrier(0);
+      probs();
+    } else {
+      probs();
+      __builtin_amdgcn_sched_barrier(0);
+      products();
+    }
+    // A second pass runs only after the reference moved (see kF8SumLimit);
+    // the rescale of the accumulator then follows the P V product of tile
+    // j-1, which was taken against the old reference.  The bit-pattern test
+    // on the next tile's scores (a NaN) is never true for finite inputs;
+    // reading them here keeps their MFMAs ahead of the branch.
+    bool bad = !(t0 + t1 < kF8SumLimit);
 #pragma unroll
-      for (int kb = 0; kb < S::KB; ++kb) bad = bad || __builtin_bit_cast(int, sn[kb][15]) == -1;
-      if (__builtin_expect(!__any(bad) || pass > 0, 1)) break;
+    for (int kb = 0; kb < S::KB; ++kb) bad = bad || __builtin_bit_cast(int, sn[kb][15]) == -1;
+    if (__builtin_expect(__any(bad), 0)) {
       const float m_new = fmaxf(m_run, tile_max(sc));
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run[0] *= alpha;
@@ -298,35 +387,67 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       m_run = m_new;
+      probs();
     }
     l_run[0] += t0;
     l_run[1] += t1;
-#pragma unroll
-    for (int db = 0; db < S::DB; ++db) {
-      v8i a;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) v2i*)(vr + voff[db] + 16 * u * S::RB));
-        a[2 * u] = t[0];
-        a[2 * u + 1] = t[1];
-      }
-      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf, oacc[db], 0, 0, 0, 127, 0, 127);
-    }
-    __syncthreads();
+    pf = pn;
+    // Step barrier: this wave's copies of the previous step are complete
+    // (vmcnt <= the copies issued here) and its LDS reads are done
+    // (lgkmcnt 0); the signal fences keep the compiler from moving memory
+    // operations across the barrier.
+    constexpr int kInFlight = 2 * S::LOADS;
+    static_assert(kInFlight < 64, "vmcnt field");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt((kInFlight & 15) | ((kInFlight >> 4) << 14) | (7 << 4));
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
 
   f32x16 sa[S::KB], sb[S::KB];
-  f8_load_tile<D, NW>(kbase, 0, p.Nk, kb0, wave, lane);
-  f8_load_tile<D, NW>(vbase, 0, p.Nk, vb0, wave, lane);
-  if (nkt > 1) f8_load_tile<D, NW>(kbase, BN, p.Nk, kb1, wave, lane);
+  load(kbase, 0, kb0);
+  load(vbase, 0, vb0);
+  load(kbase, 1, kb1);
+  load(kbase, 2, kb2);
   __syncthreads();
   s_tile(kb0, sa);
   __syncthreads();
-  for (int j = 0; j < nkt; j += 2) {
-    step(kb1, vb0, kb0, vb1, sa, sb, j);
-    if (j + 1 < nkt) step(kb0, vb1, kb1, vb0, sb, sa, j + 1);
+  // Tile t lives in K buffer t % 3 and V buffer t % 3; six steps per
+  // iteration keep every buffer choice (and the S^T register set, which
+  // alternates) a compile-time constant.
+  lds_char* const kbs[3] = {kb0, kb1, kb2};
+  lds_char* const vbs[3] = {vb0, vb1, vb2};
+  auto run = [&](auto group) {
+    for (int j0 = 0; j0 < nkt; j0 += 6) {
+      static_for<0, 6>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        const int j = j0 + u;
+        if (u == 0 || j < nkt) {
+          auto& sc = (u % 2 == 0) ? sa : sb;
+          auto& sn = (u % 2 == 0) ? sb : sa;
+          step(kbs[(u + 1) % 3], vbs[(u + 2) % 3], kbs[u % 3], vbs[(u + 1) % 3], sc, sn, j, group);
+        }
+      });
+    }
+  };
+  if ((wave >> 2) & 1)
+    run(F8Int<1>{});
+  else
+    run(F8Int<0>{});
+  // The copies of the last steps (tiles past the end) must land before the
+  // workgroup's LDS is released.
+  __builtin_amdgcn_s_waitcnt(0);
+  // P V of the last tile.  Each of its MFMAs reads operands from every lane,
+  // so it must run with the whole wave active; the empty asm statements use
+  // the accumulators here, which keeps the compiler from sinking the
+  // products into the row-predicated store below.
+  {
+    const int last = nkt - 1;
+    const lds_char* vl = last % 3 == 0 ? vb0 : last % 3 == 1 ? vb1 : vb2;
+    pv(vl, pf);
   }
+#pragma unroll
+  for (int db = 0; db < S::DB; ++db) asm volatile("" : "+v"(oacc[db]));
 
   const float l_tot = f8_half_sum(l_run[0] + l_run[1]);
   if (row < p.Nq) {
@@ -355,10 +476,13 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
     using Sh = fa::F8Shape<D, NW>;                                                     \
     __shared__ __attribute__((aligned(1024))) char k0[Sh::TILE];                       \
     __shared__ __attribute__((aligned(1024))) char k1[Sh::TILE];                       \
+    __shared__ __attribute__((aligned(1024))) char k2[Sh::TILE];                       \
     __shared__ __attribute__((aligned(1024))) char v0[Sh::TILE];                       \
     __shared__ __attribute__((aligned(1024))) char v1[Sh::TILE];                       \
+    __shared__ __attribute__((aligned(1024))) char v2[Sh::TILE];                       \
     fa::fwd_fp8_body<D, NW, CAUSAL>(p, (fa::lds_char*)k0, (fa::lds_char*)k1,           \
-                                    (fa::lds_char*)v0, (fa::lds_char*)v1);             \
+                                    (fa::lds_char*)k2, (fa::lds_char*)v0,              \
+                                    (fa::lds_char*)v1, (fa::lds_char*)v2);             \
   }
 
 FA_FWD_FP8_KERNEL(fa_fwd_fp8_d64_nomask, 64, 8, false)
