@@ -404,6 +404,19 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
 
+  // The V buffers start as zeros: a copy through a resource of fewer rows
+  // leaves the LDS rows past them as they were, and those rows meet
+  // probability 0 in the P V product, which stays 0 only for finite values
+  // (stale rows of earlier tiles are finite; LDS never written may not be).
+  {
+    using v4 = unsigned __attribute__((ext_vector_type(4)));
+    for (int i = tid; i < S::TILE / 16; i += 64 * NW) {
+      *(__attribute__((address_space(3))) v4*)(vb0 + 16 * i) = v4{};
+      *(__attribute__((address_space(3))) v4*)(vb1 + 16 * i) = v4{};
+      *(__attribute__((address_space(3))) v4*)(vb2 + 16 * i) = v4{};
+    }
+    __syncthreads();
+  }
   f32x16 sa[S::KB], sb[S::KB];
   load(kbase, 0, kb0);
   load(vbase, 0, vb0);
