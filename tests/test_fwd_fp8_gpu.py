@@ -65,6 +65,12 @@ ODD = [
     (1, 8, 4, 300, 1100, 128, False),
     (1, 8, 2, 1000, 2100, 128, False),
     (2, 4, 4, 129, 700, 64, False),
+    # one, two and three key tiles: fewer tiles than the kernel's copy
+    # pipeline is deep (the products of the last tile run after the loop)
+    (1, 2, 1, 64, 64, 128, True),
+    (1, 2, 2, 40, 120, 128, False),
+    (1, 3, 1, 200, 130, 64, False),
+    (1, 2, 1, 190, 190, 128, True),
 ]
 
 
