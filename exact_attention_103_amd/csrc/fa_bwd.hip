@@ -193,12 +193,30 @@ __device__ __forceinline__ bf16x8 row_read(const lds_char* t, int r, int c) {
 // ---------------------------------------------------------------------------
 // dQ (and Delta)
 // ---------------------------------------------------------------------------
+// Compile-time loop (every unrolled step's LDS stages are then constants).
+template <int I>
+struct BwdInt {
+  static constexpr int value = I;
+};
+template <int I, int N, typename F>
+__device__ __forceinline__ void bwd_static_for(F&& f) {
+  if constexpr (I < N) {
+    f(BwdInt<I>{});
+    bwd_static_for<I + 1, N>(f);
+  }
+}
+
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, lds_char* kb0, lds_char* kb1,
-                                            lds_char* vb0, lds_char* vb1) {
+                                            lds_char* kb2, lds_char* vb0, lds_char* vb1,
+                                            lds_char* vb2) {
   using S = BwdShape<D>;
   constexpr int BN = dq_keys<D>(), BM = kDqRows;
   constexpr int KB = BN / 32, KC = BN / 16;
+  // At d = 256 (one wave per SIMD) the K/V tiles are copied two steps ahead
+  // into three stages and a step's barrier waits only for the previous
+  // step's copies, as in the dK/dV kernel.
+  constexpr bool kThree = D == 256;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -272,7 +290,10 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, lds_char* kb0, l
   auto step = [&](const lds_char* kr, const lds_char* vr, lds_char* kw, lds_char* vw, int j) {
     const int j0 = j * BN;
     FA_STAGE_FENCE();
-    if (j + 1 < nkt) {
+    if (kThree) {
+      dma_tile<D, BN>(rows_rsrc<D, BN>(kbase, j0 + 2 * BN, p.Nk), doff, kw, wave);
+      dma_tile<D, BN>(rows_rsrc<D, BN>(vbase, j0 + 2 * BN, p.Nk), doff, vw, wave);
+    } else if (j + 1 < nkt) {
       dma_tile<D, BN>(rows_rsrc<D, BN>(kbase, j0 + BN, p.Nk), doff, kw, wave);
       dma_tile<D, BN>(rows_rsrc<D, BN>(vbase, j0 + BN, p.Nk), doff, vw, wave);
     }
@@ -306,15 +327,46 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, lds_char* kb0, l
         dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb, dq[db], 0, 0, 0);
       }
     }
-    __syncthreads();
+    if constexpr (kThree) {
+      // This wave's copies of the previous step are complete (vmcnt <= the
+      // copies issued in this step), its LDS reads are done; the signal
+      // fences keep the compiler from moving memory operations across.
+      constexpr int L = 2 * Dma<D, BN, kBwdWaves>::LOADS;
+      static_assert(L < 64, "vmcnt field");
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt((L & 15) | ((L >> 4) << 14) | (7 << 4));
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    } else {
+      __syncthreads();
+    }
   };
 
   dma_tile<D, BN>(rows_rsrc<D, BN>(kbase, 0, p.Nk), doff, kb0, wave);
   dma_tile<D, BN>(rows_rsrc<D, BN>(vbase, 0, p.Nk), doff, vb0, wave);
-  __syncthreads();
-  for (int j = 0; j < nkt; j += 2) {
-    step(kb0, vb0, kb1, vb1, j);
-    if (j + 1 < nkt) step(kb1, vb1, kb0, vb0, j + 1);
+  if constexpr (kThree) {
+    // Tile j lives in stage j % 3; step j copies tile j + 2 (tiles past Nk
+    // read zero rows, so every step issues the same number of copies).
+    dma_tile<D, BN>(rows_rsrc<D, BN>(kbase, BN, p.Nk), doff, kb1, wave);
+    dma_tile<D, BN>(rows_rsrc<D, BN>(vbase, BN, p.Nk), doff, vb1, wave);
+    __syncthreads();
+    lds_char* const kbs[3] = {kb0, kb1, kb2};
+    lds_char* const vbs[3] = {vb0, vb1, vb2};
+    for (int j0 = 0; j0 < nkt; j0 += 3) {
+      bwd_static_for<0, 3>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if (u == 0 || j0 + u < nkt)
+          step(kbs[u], vbs[u], kbs[(u + 2) % 3], vbs[(u + 2) % 3], j0 + u);
+      });
+    }
+    // No copy into this workgroup's LDS may still be in flight when it ends.
+    __builtin_amdgcn_s_waitcnt(0);
+  } else {
+    __syncthreads();
+    for (int j = 0; j < nkt; j += 2) {
+      step(kb0, vb0, kb1, vb1, j);
+      if (j + 1 < nkt) step(kb1, vb1, kb0, vb0, j + 1);
+    }
   }
 
   // dQ = scale * acc, bf16 (round to nearest even); lane holds d rows
@@ -353,19 +405,6 @@ struct DkvStage {
   static constexpr int TILE3 = D == 256 ? TILE : 16;
   static constexpr int STATS3 = D == 256 ? STATS : 16;
 };
-
-// Compile-time loop (every unrolled step's LDS stages are then constants).
-template <int I>
-struct BwdInt {
-  static constexpr int value = I;
-};
-template <int I, int N, typename F>
-__device__ __forceinline__ void bwd_static_for(F&& f) {
-  if constexpr (I < N) {
-    f(BwdInt<I>{});
-    bwd_static_for<I + 1, N>(f);
-  }
-}
 
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* qt0, lds_char* qt1,
@@ -593,12 +632,15 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* qt0,
 #define FA_BWD_DQ(D, CAUSAL, NAME, WPE)                                                    \
   extern "C" __global__ void __launch_bounds__(64 * fa::kBwdWaves, WPE) NAME(fa::BwdParams p) { \
     constexpr int T = fa::dq_keys<D>() * 2 * D;                                            \
+    constexpr int T3 = D == 256 ? T : 16; /* third stage at d = 256 only */                \
     __shared__ __attribute__((aligned(1024))) char k0[T];                                  \
     __shared__ __attribute__((aligned(1024))) char k1[T];                                  \
+    __shared__ __attribute__((aligned(1024))) char k2[T3];                                 \
     __shared__ __attribute__((aligned(1024))) char v0[T];                                  \
     __shared__ __attribute__((aligned(1024))) char v1[T];                                  \
-    fa::bwd_dq_body<D, CAUSAL>(p, (fa::lds_char*)k0, (fa::lds_char*)k1, (fa::lds_char*)v0, \
-                               (fa::lds_char*)v1);                                         \
+    __shared__ __attribute__((aligned(1024))) char v2[T3];                                 \
+    fa::bwd_dq_body<D, CAUSAL>(p, (fa::lds_char*)k0, (fa::lds_char*)k1, (fa::lds_char*)k2, \
+                               (fa::lds_char*)v0, (fa::lds_char*)v1, (fa::lds_char*)v2);   \
   }
 
 #define FA_BWD_DKDV(D, CAUSAL, NAME, WPE)                                                  \
