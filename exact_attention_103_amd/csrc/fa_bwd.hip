@@ -328,15 +328,8 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, lds_char* kb0, l
       }
     }
     if constexpr (kThree) {
-      // This wave's copies of the previous step are complete (vmcnt <= the
-      // copies issued in this step), its LDS reads are done; the signal
-      // fences keep the compiler from moving memory operations across.
-      constexpr int L = 2 * Dma<D, BN, kBwdWaves>::LOADS;
-      static_assert(L < 64, "vmcnt field");
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __builtin_amdgcn_s_waitcnt((L & 15) | ((L >> 4) << 14) | (7 << 4));
-      __builtin_amdgcn_s_barrier();
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      // Only the copies issued in this step (K and V tiles) may be in flight.
+      copies_in_flight_barrier<2 * Dma<D, BN, kBwdWaves>::LOADS>();
     } else {
       __syncthreads();
     }
@@ -562,19 +555,14 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, lds_char* qt0,
           tr_read(qt, toff[db], toff[db] + 16 * S::RB), sb, dk[db], 0, 0, 0);
     }
     if constexpr (kThree) {
-      // This wave's copies of the previous step are complete (vmcnt <= the
-      // copies issued in this step: two tiles, and the stats on wave 0),
-      // its LDS reads are done; the signal fences keep the compiler from
-      // moving memory operations across the barrier.
+      // Only the copies issued in this step may be in flight: the Q and dO
+      // tiles, and on wave 0 the stats.
       constexpr int L = 2 * Dma<D, BM, NW>::LOADS;
-      static_assert(L + 1 < 64, "vmcnt field");
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
       if (wave == 0)
-        __builtin_amdgcn_s_waitcnt(((L + 1) & 15) | (((L + 1) >> 4) << 14) | (7 << 4));
+        wait_copies_in_flight<L + 1>();
       else
-        __builtin_amdgcn_s_waitcnt((L & 15) | ((L >> 4) << 14) | (7 << 4));
-      __builtin_amdgcn_s_barrier();
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        wait_copies_in_flight<L>();
+      step_barrier();
     } else {
       __syncthreads();
     }

@@ -392,16 +392,9 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
     l_run[0] += t0;
     l_run[1] += t1;
     pf = pn;
-    // Step barrier: this wave's copies of the previous step are complete
-    // (vmcnt <= the copies issued here) and its LDS reads are done
-    // (lgkmcnt 0); the signal fences keep the compiler from moving memory
-    // operations across the barrier.
-    constexpr int kInFlight = 2 * S::LOADS;
-    static_assert(kInFlight < 64, "vmcnt field");
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt((kInFlight & 15) | ((kInFlight >> 4) << 14) | (7 << 4));
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    // Step barrier: only this step's copies (a K and a V tile) may be in
+    // flight past it.
+    copies_in_flight_barrier<2 * S::LOADS>();
   };
 
   // The V buffers start as zeros: a copy through a resource of fewer rows

@@ -44,6 +44,30 @@ constexpr int kCachePolicyNT = 2;
   } while (0)
 #endif
 
+// Step barrier of kernels that issue their LDS copies two steps ahead: the
+// wave waits until at most N of its vector-memory operations are in flight
+// (the copies it issued in this step, which may land later) and its LDS
+// operations are done, then every wave of the workgroup meets.  A plain
+// __syncthreads would also wait for this step's copies.  The signal fences
+// keep the compiler from moving memory operations across the barrier.  The
+// immediate is gfx9's s_waitcnt encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt (7: no wait) in bits 6:4, lgkmcnt (0) in bits 11:8.
+template <int N>
+__device__ __forceinline__ void wait_copies_in_flight() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+__device__ __forceinline__ void step_barrier() {
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+template <int N>
+__device__ __forceinline__ void copies_in_flight_barrier() {
+  wait_copies_in_flight<N>();
+  step_barrier();
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
