@@ -27,7 +27,9 @@ same stream, inputs already resident in HBM.  Prints one JSON line:
             kernel name, median TFLOP/s and roofline: the MFMA peak for
             d >= 128, the VALU softmax bound (see alu_peak_tflops) for d <= 64
   sclk      shader clock samples (amd-smi) taken during a sustained run of
-            the prefill after the timed steps
+            the prefill after the timed steps; amd-smi's reading lags the
+            load (it can still show the idle clock in the first second), so
+            only samples from the second half of a 3 s run count
 
 Every timed series is preceded by a warm-up of at least 200 ms of the same
 launches (and at least --warmup steps): the clock ramps up over the first
@@ -369,10 +371,12 @@ def _under_profiler():
     return "rocprof" in pre or any(k.startswith("ROCPROF") for k in os.environ)
 
 
-def sample_sclk(call, seconds=1.0):
+def sample_sclk(call, seconds=3.0):
     """Shader clock (MHz) samples from amd-smi while `call` runs back to back
-    for about `seconds`.  Returns the samples' median/min/max, or a note with
-    the start of amd-smi's reply when no clock could be read from it."""
+    for about `seconds`.  amd-smi's value lags the load, so only the samples
+    taken in the second half of the run count.  Returns their median/min/max
+    (and how many samples were dropped), or a note with the start of
+    amd-smi's reply when no clock could be read from it."""
     import re
     import subprocess
     import threading
@@ -392,7 +396,7 @@ def sample_sclk(call, seconds=1.0):
             m = re.search(r'"gfx_0"\s*:\s*\{.*?"clk"\s*:\s*\{\s*"value"\s*:\s*(\d+)', text,
                           re.S | re.I)
             if m:
-                samples.append(int(m.group(1)))
+                samples.append((time.perf_counter(), int(m.group(1))))
             elif not raw:
                 raw.append((text or r.stderr)[:300])
 
@@ -405,10 +409,12 @@ def sample_sclk(call, seconds=1.0):
         torch.cuda.synchronize()
     stop.set()
     th.join(timeout=10)
-    if not samples:
+    late = [v for t, v in samples if t >= t0 + seconds / 2]
+    if not late:
         return {"mhz_median": None, "note": "no clock parsed", "reply": raw[:1]}
-    return {"mhz_median": float(np.median(samples)), "mhz_min": min(samples),
-            "mhz_max": max(samples), "samples": len(samples), "source": " ".join(cmd)}
+    return {"mhz_median": float(np.median(late)), "mhz_min": min(late),
+            "mhz_max": max(late), "samples": len(late),
+            "samples_dropped_first_half": len(samples) - len(late), "source": " ".join(cmd)}
 
 
 def main():
