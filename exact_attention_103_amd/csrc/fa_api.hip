@@ -68,7 +68,7 @@ int fwd_fp8_common(const void* q, const void* k, const void* v, void* o, float* 
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
   if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
   if (causal && Nq > Nk) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_HEAD_DIM;
   if (!scale_ok(scale)) return FA_ERR_SCALE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_ALIGN;
@@ -78,7 +78,7 @@ int fwd_fp8_common(const void* q, const void* k, const void* v, void* o, float* 
   const int64_t kv_bytes = checked_product({B, Hkv, Nk, d});
   const int64_t o_bytes = checked_product({B, Hq, Nq, d, 2});
   const int64_t lse_bytes = checked_product({B, Hq, Nq, 4});
-  const int bm = fa::fwd_fp8_rows_per_block();
+  const int bm = fa::fwd_fp8_rows_per_block(d);
   const int64_t grid = checked_product({(Nq + bm - 1) / bm, B, Hq});
   if (q_bytes < 0 || kv_bytes < 0 || o_bytes < 0 || lse_bytes < 0 || grid < 0 ||
       grid > INT32_MAX)
@@ -498,7 +498,7 @@ const char* fa_strerror(int status) {
     case FA_OK: return "success";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid shape (sizes must be > 0, Hq a multiple of Hkv, causal needs Nq <= Nk)";
-    case FA_ERR_HEAD_DIM: return "unsupported head dimension (32, 64, 128 or 256; fp8 forward: 64 or 128)";
+    case FA_ERR_HEAD_DIM: return "unsupported head dimension (32, 64, 128 or 256; fp8 forward: 64, 128 or 256)";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case FA_ERR_WORKSPACE: return "workspace is NULL or too small";
     case FA_ERR_SPLITS: return "num_splits out of range";

@@ -175,7 +175,7 @@ int quant_blocks(int rows, int d);
 const char* quant_kernel_name(int d, int stage);
 hipError_t launch_quant(const QuantParams& p, int d, hipStream_t s);
 const char* fwd_fp8_kernel_name(int d, bool causal);
-int fwd_fp8_rows_per_block();
+int fwd_fp8_rows_per_block(int d);
 const char* bwd_kernel_name(int d, bool causal, int stage);
 bool bwd_supported_d(int d);
 int bwd_dq_grid_blocks(int B, int Hq, int Nq);

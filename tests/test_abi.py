@@ -126,6 +126,8 @@ def test_serve_helpers():
 def test_fp8_names_and_quantiser():
     assert fa.fa_fwd_fp8_kernel_name(128, 1) == "fa_fwd_fp8_d128_causal"
     assert fa.fa_fwd_fp8_kernel_name(64, 0) == "fa_fwd_fp8_d64_nomask"
+    assert fa.fa_fwd_fp8_kernel_name(256, 1) == "fa_fwd_fp8_d256_causal"
+    assert fa.fa_fwd_fp8_kernel_name(256, 0) == "fa_fwd_fp8_d256_nomask"
     assert fa.fa_fwd_fp8_kernel_name(32, 0) is None
     assert fa.fa_fwd_fp8_kernel_name(128, 2) is None
 
@@ -336,7 +338,7 @@ def test_serve_rejects(kw, code):
 @cpu_only
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), -1), (dict(o=0), -1), (dict(B=0), -2), (dict(Hq=3), -2), (dict(causal=2), -2),
-    (dict(Nq=65, Nk=64), -2), (dict(d=32), -3), (dict(d=256), -3),
+    (dict(Nq=65, Nk=64), -2), (dict(d=32), -3), (dict(d=96), -3),
     (dict(scale=0.0), -8), (dict(qd=0.0), -8), (dict(kd=math.inf), -8), (dict(vd=-1.0), -8),
     (dict(q=Q + 8), -4), (dict(o=O + 4), -4),
     (dict(o=Q), -9), (dict(lse=K + 16), -9),

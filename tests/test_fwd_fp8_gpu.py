@@ -71,6 +71,14 @@ ODD = [
     (1, 2, 2, 40, 120, 128, False),
     (1, 3, 1, 200, 130, 64, False),
     (1, 2, 1, 190, 190, 128, True),
+    # d = 256 (16 rows per wave, 128-key tiles): tails, GQA, Nq < Nk, one
+    # valid row in the last query block, head-major non-causal order
+    (1, 2, 1, 200, 200, 256, False),
+    (1, 2, 1, 200, 200, 256, True),
+    (1, 4, 2, 77, 300, 256, True),
+    (1, 2, 1, 129, 190, 256, False),
+    (2, 2, 2, 130, 130, 256, True),
+    (1, 8, 4, 300, 1100, 256, False),
 ]
 
 
@@ -121,8 +129,12 @@ def test_fp8_train_sampled():
     _workload("train_c", [(3, 5)], 256)
 
 
+def test_fp8_sweep_d256_sampled():
+    _workload("sweep_d256", [(0, 0), (1, 13)], 256)
+
+
 @pytest.mark.parametrize("slope", [0.2, 1.0, -1.0])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_fp8_drifting_scores(slope, d):
     """Rising scores exceed the reference maximum by far more than 2^8 in
     tile after tile, so the tile's probabilities are redone against a new

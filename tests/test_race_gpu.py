@@ -93,7 +93,8 @@ def test_fwd_matches_serial_build(shape, serial_lib, monkeypatch):
 FP8 = [(1, 4, 2, 1000, 1000, 64, True), (1, 2, 1, 3000, 3000, 128, True),
        (1, 2, 2, 300, 1100, 128, False),
        (1, 8, 4, 300, 1100, 128, False),    # head-major XCD order
-       (1, 2, 1, 190, 190, 128, True), (1, 2, 2, 40, 120, 64, False)]   # 2-3 key tiles
+       (1, 2, 1, 190, 190, 128, True), (1, 2, 2, 40, 120, 64, False),   # 2-3 key tiles
+       (1, 4, 2, 700, 1000, 256, True), (1, 8, 4, 300, 1100, 256, False)]
 
 
 @pytest.mark.parametrize("shape", FP8, ids=[
