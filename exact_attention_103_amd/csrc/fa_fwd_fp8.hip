@@ -150,6 +150,14 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+template <int I, int N, typename F>
+__device__ __forceinline__ void f8_static_for(F&& f) {
+  if constexpr (I < N) {
+    f(F8Int<I>{});
+    f8_static_for<I + 1, N>(f);
+  }
+}
+
 __device__ __forceinline__ v8i f8_mfma_operand(v4i lo, v4i hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
@@ -684,7 +692,6 @@ __device__ __forceinline__ void fwd_fp8_wide_body(const FwdF8Params& p, lds_char
         sacc[kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f8_mfma_operand(lo, hi), qf[t],
                                                                    sacc[kb], 0, 0, 0, 127, 0, 127);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
   auto needs_mask = [&](int t) {
@@ -719,7 +726,6 @@ __device__ __forceinline__ void fwd_fp8_wide_body(const FwdF8Params& p, lds_char
         a[2 * u + 1] = t[1];
       }
       oacc[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, pft, oacc[db], 0, 0, 0, 127, 0, 127);
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -770,6 +776,18 @@ __device__ __forceinline__ void fwd_fp8_wide_body(const FwdF8Params& p, lds_char
     l_run[1] += t1;
     pv(vr, pf);
     s_tile(kr, sn);
+    // Each MFMA's LDS operand reads are issued one product ahead, and no
+    // further: P V (four transposing reads each), then S^T (two reads each).
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    f8_static_for<0, S::DB>([&](auto c) {
+      __builtin_amdgcn_sched_group_barrier(0x100, decltype(c)::value + 1 < S::DB ? 4 : 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    });
+    f8_static_for<0, S::KB * S::KSTEPS>([&](auto c) {
+      if constexpr (decltype(c)::value + 1 < S::KB * S::KSTEPS)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    });
     __syncthreads();
   };
 
