@@ -601,12 +601,15 @@ __device__ __forceinline__ void fwd_fp8_wide_body(const FwdF8Params& p, lds_char
   // there.  K: row P / CPR, swizzled chunk P % CPR.  V: P decodes into a
   // 16-row group a, row b and chunk c of the padded layout; padding chunks
   // (and the blocks past the tile) re-read the group's first chunk.
-  int koffs[S::KLOADS], voffs[S::VLOADS];
-#pragma unroll
-  for (int i = 0; i < S::KLOADS; ++i) {
-    const int P = (i * NW + wave) * 64 + lane;
+  // K: the swizzle of row r only depends on r mod 16, which is the same
+  // for a lane in all of its blocks (they are 8 KB apart), so one per-lane
+  // offset serves every load (the block's offset goes in the scalar operand).
+  int voffs[S::VLOADS];
+  int koff0;
+  {
+    const int P = wave * 64 + lane;
     const int r = P / S::CPR, q = P % S::CPR;
-    koffs[i] = r * S::RB + ((q ^ w_kx(r)) << 4);
+    koff0 = r * S::RB + ((q ^ w_kx(r)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < S::VLOADS; ++i) {
@@ -622,7 +625,7 @@ __device__ __forceinline__ void fwd_fp8_wide_body(const FwdF8Params& p, lds_char
     for (int i = 0; i < S::KLOADS; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, (__attribute__((address_space(3))) void*)(tile + (i * NW + wave) * 1024), 16,
-          koffs[i], 0, 0, 0);
+          koff0, i * NW * 1024, 0, 0);
   };
   auto load_v = [&](int t, lds_char* tile) {
     const int rows = t < nkt ? min(p.Nk - t * BN, BN) : 0;
