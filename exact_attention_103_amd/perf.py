@@ -97,7 +97,7 @@ def main():
                           "pct_of_2500": round(100 * flop / ms / 1e9 / 2500, 1)}), flush=True)
         del q, k, v, do, o, lse, ws
     for name, B, H, N, d, causal, sc in FWD:
-        if d not in (64, 128):
+        if d not in (64, 128, 256):
             continue
         # fp8 forward on random e4m3 codes of magnitude <= 2 (speed only).
         q8 = torch.randint(0, 0x41, (B, H, N, d), dtype=torch.uint8, device="cuda")
