@@ -301,6 +301,17 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, lds_char* kb0, l
     f32x16 sacc[KB], dpacc[KB];
     xt_tile(kr, qf, sacc);    // S^T  = K Q^T
     xt_tile(vr, df, dpacc);   // dP^T = V dO^T
+    // Interleave the tile reads of both products one read ahead of the
+    // product that consumes them, so each LDS read overlaps an MFMA instead
+    // of all reads issuing up front.
+    {
+      constexpr int NM = 2 * KB * S::KSTEPS;
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 3);
+      bwd_static_for<0, NM>([&](auto c) {
+        if constexpr (decltype(c)::value + 1 < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 3);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+      });
+    }
     // Keys past Nk, or past the diagonal when causal, get P = 0.
     if ((j0 + BN > p.Nk) || (CAUSAL && j0 + BN - 1 > qw + off)) {
       const int lim = (CAUSAL ? min(p.Nk - 1, row + off) : p.Nk - 1) - j0 - 4 * hl;
