@@ -346,10 +346,10 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
     // and saves zeroing them.
     v8i pn = pf;
     float t0, t1;
+    // The sums start from the first pair: a sum started at 0.f costs an
+    // addition of zero, which the compiler keeps (it would turn -0 into +0).
     auto probs = [&]() {
       const float nm = -m_run;
-      t0 = 0.f;
-      t1 = 0.f;
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         const int kb = w >> 2, r0 = 4 * (w & 3);
@@ -357,8 +357,8 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
         const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 1], cexp, nm));
         const float e2 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 2], cexp, nm));
         const float e3 = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + 3], cexp, nm));
-        t0 += e0 + e2;
-        t1 += e1 + e3;
+        t0 = w == 0 ? e0 + e2 : t0 + (e0 + e2);
+        t1 = w == 0 ? e1 + e3 : t1 + (e1 + e3);
         int x = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, pn[w], false);
         x = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, x, true);
         pn[w] = x;
@@ -747,16 +747,14 @@ __device__ __forceinline__ void fwd_fp8_wide_body(const FwdF8Params& p, lds_char
     float t0, t1;
     for (int pass = 0;; ++pass) {
       const float nm = -m_run;
-      t0 = 0.f;
-      t1 = 0.f;
 #pragma unroll
       for (int kb = 0; kb < S::KB; ++kb) {
         const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][0], cexp, nm));
         const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][1], cexp, nm));
         const float e2 = __builtin_amdgcn_exp2f(fmaf(sc[kb][2], cexp, nm));
         const float e3 = __builtin_amdgcn_exp2f(fmaf(sc[kb][3], cexp, nm));
-        t0 += e0 + e2;
-        t1 += e1 + e3;
+        t0 = kb == 0 ? e0 + e2 : t0 + (e0 + e2);   // no addition of zero (see probs above)
+        t1 = kb == 0 ? e1 + e3 : t1 + (e1 + e3);
         int x = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, pf[kb], false);
         x = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, x, true);
         pf[kb] = x;
