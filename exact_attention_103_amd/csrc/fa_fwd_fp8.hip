@@ -27,12 +27,15 @@
 // order that the P^T registers hold.  O = v_factor * acc / l (bf16), LSE in
 // natural log of the scaled scores.
 //
-// Schedule: eight waves of 32 query rows per workgroup, one 64-key tile per
-// step.  The P V product of a tile runs one step after its probabilities,
-// and the two waves that share a SIMD issue each step's MFMAs and its
-// exponentials in opposite orders, so one wave's softmax overlaps the other
-// wave's products.  K and V tiles are copied two steps ahead into three LDS
-// buffers each, so the per-step barrier rarely waits for memory.
+// Schedule: 32 query rows per wave, one 64-key tile per step; eight waves
+// per workgroup (two per SIMD) at d = 64 and 128, four (one per SIMD) at
+// d = 256, where O^T alone takes 128 registers.  The P V product of a tile
+// runs one step after its probabilities.  Two waves that share a SIMD issue
+// each step's MFMAs and its exponentials in opposite orders, so one wave's
+// softmax overlaps the other wave's products; a wave alone on its SIMD
+// (d = 256) leaves both halves to the compiler, which interleaves them.  K
+// and V tiles are copied two steps ahead into three LDS buffers each, so
+// the per-step barrier rarely waits for memory.
 
 #include "fa_internal.h"
 
@@ -79,13 +82,19 @@ struct F8Shape {
 //  * the V^T operand (8-bit transposing 8-byte reads, 32 lanes per pass):
 //    rows {0..3, 8..11} + 4h, chunks 2db and 2db + 1, so the rows of one
 //    line position must differ in X's bit 1.
-// 128-byte rows (two per line): X = i with its two low bits swapped,
-// i = (r / 2) mod 8; 64-byte rows (four per line): X = (r / 4) mod 4.  Both
-// touch every bank once per pass in either pattern (an earlier X = i put two
-// lanes on each bank of the V^T reads).
+// 256-byte rows (one per line): X is the bit permutation of r mod 16 that
+// takes r's bits 2, 0, 1, 3 to X's bits 0, 1, 2, 3 -- a bijection on 16
+// consecutive rows (K), and X / 2 differs across rows {0..3, 8..11} + 4h
+// (V^T).  128-byte rows (two per line): X = i with its two low bits
+// swapped, i = (r / 2) mod 8; 64-byte rows (four per line): X = (r / 4) mod
+// 4.  All three touch every bank once per pass in either pattern (an
+// earlier X = i put two lanes on each bank of the V^T reads, and the
+// 128-byte rule on 256-byte rows two on each bank of the K reads).
 template <int RB>
 __device__ __forceinline__ int f8_xor(int r) {
-  if constexpr (RB >= 128) {
+  if constexpr (RB >= 256) {
+    return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
+  } else if constexpr (RB == 128) {
     const int i = (r >> 1) & 7;
     return ((i & 1) << 1) | ((i >> 1) & 1) | (i & 4);
   } else {
@@ -147,14 +156,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (I < N) {
     f(F8Int<I>{});
     static_for<I + 1, N>(f);
-  }
-}
-
-template <int I, int N, typename F>
-__device__ __forceinline__ void f8_static_for(F&& f) {
-  if constexpr (I < N) {
-    f(F8Int<I>{});
-    f8_static_for<I + 1, N>(f);
   }
 }
 
@@ -319,7 +320,10 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
   // and w+4 of the workgroup) take the two halves in opposite orders (wave
   // group G = 1: products, then probabilities; G = 0: probabilities, then
   // products), so that one wave's exponentials run while the other wave's
-  // MFMAs do.  A scheduling barrier keeps each order as written.
+  // MFMAs do.  A scheduling barrier keeps each order as written.  With four
+  // waves (d = 256) each wave has its SIMD to itself: both halves then form
+  // one scheduling region and the compiler interleaves the wave's MFMAs with
+  // its own exponentials (+14% to +15% over the fixed order at d = 256).
   //
   // Buffers: K_{j+1} and V_{j-1} are read here; K_{j+3} is loaded over K_j
   // (read in the previous step) and V_{j+1} over V_{j-2}.  Every copy is
@@ -368,7 +372,10 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
       s_tile(kr, sn);
       if (j > 0) pv(vprev, pf);
     };
-    if constexpr (decltype(group)::value) {
+    if constexpr (NW == 4) {
+      products();
+      probs();
+    } else if constexpr (decltype(group)::value) {
       products();
       __builtin_amdgcn_sched_barrier(0);
       probs();
@@ -444,7 +451,7 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
       });
     }
   };
-  if ((wave >> 2) & 1)
+  if (NW == 8 && ((wave >> 2) & 1))
     run(F8Int<1>{});
   else
     run(F8Int<0>{});
@@ -483,351 +490,11 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
 }
 
 
-// ---------------------------------------------------------------------------
-// d = 256: 16 query rows per wave on v_mfma_scale_f32_16x16x128_f8f6f4.
-//
-// At d = 256 the 32-row layout above would need 128 registers for O^T
-// alone.  Here each wave owns 16 query rows (one per lane column n =
-// lane % 16; the lane's 16-lane group G = lane / 16 is its k group), eight
-// waves share 128-key K/V tiles, and both products use the 16x16x128 fp8
-// product.  An in-bounds probe on random e4m3 operands matched the CPU
-// product with: A lane l byte p = (row l % 16, k = 32(l / 16) + p), B the
-// same with the column, and result element (m, n) in lane n + 16(m / 4),
-// register m % 4.
-//   S^T = K Q^T   A: K rows 16kb + n, d bytes 128t + 32G .. +31 (two 16-byte
-//                 LDS reads); B: Q^T of the lane's row, kept in registers.
-//                 Lane (G, n) receives keys 16kb + 4G + r (r < 4) of row n.
-//   P^T           those 32 probabilities as fp8, byte p = 4kb + r: this
-//                 lane group's k set for the P V product.
-//   O^T += V^T P^T  A: V^T rows d = 16db + (lane % 16) over the same k set,
-//                 from four 8-bit transposing reads (below).
-// The row maximum and row sum combine the four lanes of a row (one per
-// group).  Everything else (tile loop, masking, scales, the sum-triggered
-// rescale) is as in the 32-row kernel.
-struct F8Wide {
-  static constexpr int D = 256, NW = 8, RPW = 16, BM = RPW * NW;   // 128 rows per workgroup
-  static constexpr int BN = 128;           // keys per tile (one P V k-step)
-  static constexpr int RB = D;             // bytes per K or V row
-  static constexpr int CPR = D / 16;       // 16-byte chunks per row
-  static constexpr int KB = BN / 16;       // 16-key blocks of S^T
-  static constexpr int KSTEPS = D / 128;   // k-steps of S^T over d
-  static constexpr int DB = D / 16;        // 16-row d blocks of O^T
-  static constexpr int TILE = BN * RB;     // K tile (swizzled, unpadded)
-  static constexpr int KBLKS = TILE / 1024;
-  static constexpr int KLOADS = KBLKS / NW;
-  // V tile: rows padded to 17 chunks and every 16 rows by 8 more chunks.
-  static constexpr int VRB = RB + 16;                    // bytes per V row
-  static constexpr int VGRP = 16 * VRB + 128;            // bytes per 16 V rows
-  static constexpr int VCH = BN / 16 * VGRP / 16;        // chunks per V tile (2240)
-  static constexpr int VBLKS = (VCH + 63) / 64;          // 1 KB blocks (35)
-  static constexpr int VLOADS = (VBLKS + NW - 1) / NW;   // per wave (5)
-  static constexpr int VTILE = VLOADS * NW * 1024;       // LDS bytes per V buffer
-  static_assert(KBLKS % NW == 0, "whole 1 KB blocks per wave");
-};
-
-// LDS layouts.
-//  K: 16-byte chunk c of row r at c ^ (r mod 16).  An S^T operand read has
-//     the 16 lanes of a group read one chunk of 16 consecutive rows: 16
-//     different bank positions.  The rows' addresses differ by constants,
-//     so a read is a per-lane offset plus an immediate.
-//  V: row r at r*VRB + 128*(r / 16), unswizzled.  Chunk c of row 16a + b
-//     then sits at bank position (8a + b + c) mod 16.  A transposing read has
-//     the 32 lanes of two groups address chunk db of the 16 rows
-//     {16a + b : b < 8, a = 2u or 2u + 1}: 16 different positions.  Row,
-//     read and d block enter the address as immediates.
-__device__ __forceinline__ int w_kx(int r) { return r & 15; }
-__device__ __forceinline__ int w_vrow(int r) { return r * F8Wide::VRB + 128 * (r >> 4); }
-
-// Maximum and sum over the four lanes of a row (lanes l, l^16, l^32, l^48).
-__device__ __forceinline__ float f8_group4_max(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float f8_group4_sum(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-template <bool CAUSAL>
-__device__ __forceinline__ void fwd_fp8_wide_body(const FwdF8Params& p, lds_char* kb0,
-                                                  lds_char* kb1, lds_char* vb0, lds_char* vb1) {
-  using S = F8Wide;
-  constexpr int D = S::D, BN = S::BN, NW = S::NW;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int grp = lane >> 4;   // k group of the MFMA operands
-  const int n = lane & 15;     // query row (S^T, O^T column) of this lane
-
-  // Grid order as in the 32-row kernel.
-  const int BH = p.B * p.Hq;
-  const int nqb = (p.Nq + S::BM - 1) / S::BM;
-  int bh, qi;
-  if (!CAUSAL && BH % 8 == 0) {
-    const int x = blockIdx.x % 8, i = blockIdx.x / 8;
-    bh = x + 8 * (i / nqb);
-    qi = i % nqb;
-  } else {
-    bh = blockIdx.x % BH;
-    qi = blockIdx.x / BH;
-  }
-  const int qblk = CAUSAL ? (nqb - 1 - qi) : qi;
-  const int b = bh / p.Hq;
-  const int h = bh - b * p.Hq;
-  const int g = h / p.group;
-  const int q0 = qblk * S::BM;
-  const int qw = q0 + S::RPW * wave;
-  const int row = qw + n;
-  const int off = p.Nk - p.Nq;
-
-  float cexp = p.c, vds = p.v_descale;
-  if (p.q_ds) {
-    cexp = p.c * *p.q_ds * *p.k_ds;
-    vds = *p.v_ds;
-  }
-
-  const uint8_t* kbase = p.k + (size_t)(b * p.Hkv + g) * p.Nk * D;
-  const uint8_t* vbase = p.v + (size_t)(b * p.Hkv + g) * p.Nk * D;
-
-  int nkt = (p.Nk + BN - 1) / BN;
-  if (CAUSAL) nkt = min(nkt, (min(q0 + S::BM, p.Nq) - 1 + off) / BN + 1);
-
-  // Tile copies: wave w writes the 1 KB blocks i*NW + w; lane l of a block
-  // fills LDS chunk P = 64 * block + l with the global chunk that belongs
-  // there.  K: row P / CPR, swizzled chunk P % CPR.  V: P decodes into a
-  // 16-row group a, row b and chunk c of the padded layout; padding chunks
-  // (and the blocks past the tile) re-read the group's first chunk.
-  // K: the swizzle of row r only depends on r mod 16, which is the same
-  // for a lane in all of its blocks (they are 8 KB apart), so one per-lane
-  // offset serves every load (the block's offset goes in the scalar operand).
-  int voffs[S::VLOADS];
-  int koff0;
-  {
-    const int P = wave * 64 + lane;
-    const int r = P / S::CPR, q = P % S::CPR;
-    koff0 = r * S::RB + ((q ^ w_kx(r)) << 4);
-  }
-#pragma unroll
-  for (int i = 0; i < S::VLOADS; ++i) {
-    const int P = min((i * NW + wave) * 64 + lane, S::VCH - 1);
-    const int a = P / (S::VGRP / 16), q = P % (S::VGRP / 16);
-    const int bb = q / (S::VRB / 16), c = q % (S::VRB / 16);
-    voffs[i] = (bb < 16 && c < S::CPR) ? (16 * a + bb) * S::RB + 16 * c : 16 * a * S::RB;
-  }
-  auto load_k = [&](int t, lds_char* tile) {
-    const int rows = t < nkt ? min(p.Nk - t * BN, BN) : 0;
-    const __amdgpu_buffer_rsrc_t rs = f8_tile_rsrc<D>(kbase + (size_t)t * BN * D, rows);
-#pragma unroll
-    for (int i = 0; i < S::KLOADS; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(tile + (i * NW + wave) * 1024), 16,
-          koff0, i * NW * 1024, 0, 0);
-  };
-  auto load_v = [&](int t, lds_char* tile) {
-    const int rows = t < nkt ? min(p.Nk - t * BN, BN) : 0;
-    const __amdgpu_buffer_rsrc_t rs = f8_tile_rsrc<D>(vbase + (size_t)t * BN * D, rows);
-#pragma unroll
-    for (int i = 0; i < S::VLOADS; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(tile + (i * NW + wave) * 1024), 16,
-          voffs[i], 0, 0, 0);
-  };
-
-  // The V buffers start as zeros (rows past a short tile are left as they
-  // were, and meet probability 0).
-  {
-    using v4 = unsigned __attribute__((ext_vector_type(4)));
-    for (int i = tid; i < S::VTILE / 16; i += 64 * NW) {
-      *(__attribute__((address_space(3))) v4*)(vb0 + 16 * i) = v4{};
-      *(__attribute__((address_space(3))) v4*)(vb1 + 16 * i) = v4{};
-    }
-    __syncthreads();
-  }
-
-  // Q^T B operand: lane (G, n) holds Q[row][128t + 32G .. +31]; rows past Nq
-  // are zero.
-  v8i qf[S::KSTEPS];
-#pragma unroll
-  for (int t = 0; t < S::KSTEPS; ++t) {
-    if (row < p.Nq) {
-      const uint8_t* src = p.q + ((size_t)bh * p.Nq + row) * D + 128 * t + 32 * grp;
-      qf[t] = f8_mfma_operand(*reinterpret_cast<const v4i*>(src),
-                              *reinterpret_cast<const v4i*>(src + 16));
-    } else {
-      qf[t] = v8i{};
-    }
-  }
-
-  // K operand reads: row 16kb + n (its swizzle is n), chunks 8t + 2G and +1.
-  int koff[S::KSTEPS][2];
-#pragma unroll
-  for (int t = 0; t < S::KSTEPS; ++t)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) koff[t][hh] = n * S::RB + (((8 * t + 2 * grp + hh) ^ n) << 4);
-  // V^T operand reads: source lane s = lane % 16 of group G addresses, for
-  // read u, row 32u + 16(s / 8) + 4G + (s % 8) / 2, bytes 16db + 8(s % 2) ..
-  // +7; lane i of the group then receives d = 16db + i of the 8 rows the
-  // group's sources address, in the order of the P^T bytes 8u .. 8u+7
-  // (byte 4kb + r holds key 16kb + 4G + r).  Read u adds 2 row groups,
-  // d block db one chunk: both immediates.
-  const int s16 = lane & 15;
-  const int vlane = w_vrow(16 * (s16 >> 3) + 4 * grp + ((s16 & 7) >> 1)) + 8 * (s16 & 1);
-
-  f32x4 oacc[S::DB];
-#pragma unroll
-  for (int db = 0; db < S::DB; ++db) oacc[db] = f32x4{};
-  float m_run = -1e30f;
-  float l_run[2] = {0.f, 0.f};
-
-  auto s_tile = [&](const lds_char* kt, f32x4 (&sacc)[S::KB]) {
-#pragma unroll
-    for (int kb = 0; kb < S::KB; ++kb) {
-      sacc[kb] = f32x4{};
-#pragma unroll
-      for (int t = 0; t < S::KSTEPS; ++t) {
-        const lds_char* rp = kt + kb * 16 * S::RB;
-        const v4i lo = *(const __attribute__((address_space(3))) v4i*)(rp + koff[t][0]);
-        const v4i hi = *(const __attribute__((address_space(3))) v4i*)(rp + koff[t][1]);
-        sacc[kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f8_mfma_operand(lo, hi), qf[t],
-                                                                   sacc[kb], 0, 0, 0, 127, 0, 127);
-      }
-    }
-  };
-  auto needs_mask = [&](int t) {
-    const int t0 = t * BN;
-    return (t0 + BN > p.Nk) || (CAUSAL && t0 + BN - 1 > qw + off);
-  };
-  auto mask_tile = [&](f32x4 (&sacc)[S::KB], int t) {
-    const int lim = (CAUSAL ? min(p.Nk - 1, row + off) : p.Nk - 1) - t * BN - 4 * grp;
-#pragma unroll
-    for (int kb = 0; kb < S::KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (16 * kb + r > lim) sacc[kb][r] = -INFINITY;
-  };
-  auto tile_max = [&](const f32x4 (&sacc)[S::KB]) {
-    float x = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < S::KB; ++kb)
-      x = fmaxf(fmaxf(x, fmaxf(sacc[kb][0], sacc[kb][1])), fmaxf(sacc[kb][2], sacc[kb][3]));
-    return f8_group4_max(x) * cexp;
-  };
-  auto pv = [&](const lds_char* vt, const v8i& pft) {
-#pragma unroll
-    for (int db = 0; db < S::DB; ++db) {
-      const lds_char* va = vt + vlane + 16 * db;
-      v8i a;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) v2i*)(va + 2 * u * S::VGRP));
-        a[2 * u] = t[0];
-        a[2 * u + 1] = t[1];
-      }
-      oacc[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, pft, oacc[db], 0, 0, 0, 127, 0, 127);
-    }
-  };
-
-  // One step for tile j: mask, copy K_{j+2} and V_{j+1}, S^T of tile j+1 on
-  // the MFMA pipe next to tile j's probabilities, then P V of tile j.
-  v8i pf = v8i{};
-  auto step = [&](const lds_char* kr, const lds_char* vr, lds_char* kw, lds_char* vw,
-                  f32x4 (&sc)[S::KB], f32x4 (&sn)[S::KB], int j) {
-    if (needs_mask(j)) mask_tile(sc, j);
-    FA_STAGE_FENCE();
-    if (j + 2 < nkt) load_k(j + 2, kw);
-    if (j + 1 < nkt) load_v(j + 1, vw);
-    FA_STAGE_FENCE();
-    // P^T = 2^(S*c - m) as fp8: dword kb holds keys 16kb + 4G + 0..3.  The
-    // second pass runs only after the reference moved (see kF8SumLimit).
-    float t0, t1;
-    for (int pass = 0;; ++pass) {
-      const float nm = -m_run;
-#pragma unroll
-      for (int kb = 0; kb < S::KB; ++kb) {
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][0], cexp, nm));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][1], cexp, nm));
-        const float e2 = __builtin_amdgcn_exp2f(fmaf(sc[kb][2], cexp, nm));
-        const float e3 = __builtin_amdgcn_exp2f(fmaf(sc[kb][3], cexp, nm));
-        t0 = kb == 0 ? e0 + e2 : t0 + (e0 + e2);   // no addition of zero (see probs above)
-        t1 = kb == 0 ? e1 + e3 : t1 + (e1 + e3);
-        int x = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, pf[kb], false);
-        x = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, x, true);
-        pf[kb] = x;
-      }
-      // The bit-pattern test on the next tile's scores (a NaN) is never true
-      // for finite inputs; reading them keeps their MFMAs ahead of the branch.
-      bool bad = !(t0 + t1 < kF8SumLimit);
-      if (__builtin_expect(!__any(bad) || pass > 0, 1)) break;
-      const float m_new = fmaxf(m_run, tile_max(sc));
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run[0] *= alpha;
-      l_run[1] *= alpha;
-#pragma unroll
-      for (int db = 0; db < S::DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) oacc[db][r] *= alpha;
-      m_run = m_new;
-    }
-    l_run[0] += t0;
-    l_run[1] += t1;
-    pv(vr, pf);
-    s_tile(kr, sn);
-    // Each MFMA's LDS operand reads are issued one product ahead, and no
-    // further: P V (four transposing reads each), then S^T (two reads each).
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-    f8_static_for<0, S::DB>([&](auto c) {
-      __builtin_amdgcn_sched_group_barrier(0x100, decltype(c)::value + 1 < S::DB ? 4 : 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    });
-    f8_static_for<0, S::KB * S::KSTEPS>([&](auto c) {
-      if constexpr (decltype(c)::value + 1 < S::KB * S::KSTEPS)
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    });
-    __syncthreads();
-  };
-
-  f32x4 sa[S::KB], sb[S::KB];
-  load_k(0, kb0);
-  load_v(0, vb0);
-  if (nkt > 1) load_k(1, kb1);
-  __syncthreads();
-  s_tile(kb0, sa);
-  __syncthreads();
-  for (int j = 0; j < nkt; j += 2) {
-    step(kb1, vb0, kb0, vb1, sa, sb, j);
-    if (j + 1 < nkt) step(kb0, vb1, kb1, vb0, sb, sa, j + 1);
-  }
-  // No copy into this workgroup's LDS may still be in flight when it ends.
-  __builtin_amdgcn_s_waitcnt(0);
-
-  const float l_tot = f8_group4_sum(l_run[0] + l_run[1]);
-  if (row < p.Nq) {
-    const float inv = vds / l_tot;
-    uint16_t* orow = p.o + ((size_t)bh * p.Nq + row) * D;
-#pragma unroll
-    for (int db = 0; db < S::DB; ++db) {
-      bf16x2 lo = {(__bf16)(oacc[db][0] * inv), (__bf16)(oacc[db][1] * inv)};
-      bf16x2 hi = {(__bf16)(oacc[db][2] * inv), (__bf16)(oacc[db][3] * inv)};
-      uint2 w;
-      w.x = __builtin_bit_cast(unsigned, lo);
-      w.y = __builtin_bit_cast(unsigned, hi);
-      *reinterpret_cast<uint2*>(orow + 16 * db + 4 * grp) = w;
-    }
-    if (grp == 0) p.lse[(size_t)bh * p.Nq + row] = (m_run + log2f(l_tot)) * kLn2;
-  }
-}
-
 }  // namespace
 }  // namespace fa
 
 #define FA_FWD_FP8_KERNEL(NAME, D, NW, CAUSAL)                                          \
-  extern "C" __global__ void __launch_bounds__(64 * NW, 2) NAME(fa::FwdF8Params p) {   \
+  extern "C" __global__ void __launch_bounds__(64 * NW, NW / 4) NAME(fa::FwdF8Params p) { \
     using Sh = fa::F8Shape<D, NW>;                                                     \
     __shared__ __attribute__((aligned(1024))) char k0[Sh::TILE];                       \
     __shared__ __attribute__((aligned(1024))) char k1[Sh::TILE];                       \
@@ -844,25 +511,17 @@ FA_FWD_FP8_KERNEL(fa_fwd_fp8_d64_nomask, 64, 8, false)
 FA_FWD_FP8_KERNEL(fa_fwd_fp8_d64_causal, 64, 8, true)
 FA_FWD_FP8_KERNEL(fa_fwd_fp8_d128_nomask, 128, 8, false)
 FA_FWD_FP8_KERNEL(fa_fwd_fp8_d128_causal, 128, 8, true)
+FA_FWD_FP8_KERNEL(fa_fwd_fp8_d256_nomask, 256, 4, false)
+FA_FWD_FP8_KERNEL(fa_fwd_fp8_d256_causal, 256, 4, true)
 
-#define FA_FWD_FP8_WIDE_KERNEL(NAME, CAUSAL)                                            \
-  extern "C" __global__ void __launch_bounds__(64 * fa::F8Wide::NW, 2) NAME(           \
-      fa::FwdF8Params p) {                                                             \
-    using Sh = fa::F8Wide;                                                             \
-    __shared__ __attribute__((aligned(1024))) char k0[Sh::TILE];                       \
-    __shared__ __attribute__((aligned(1024))) char k1[Sh::TILE];                       \
-    __shared__ __attribute__((aligned(1024))) char v0[Sh::VTILE];                      \
-    __shared__ __attribute__((aligned(1024))) char v1[Sh::VTILE];                      \
-    fa::fwd_fp8_wide_body<CAUSAL>(p, (fa::lds_char*)k0, (fa::lds_char*)k1,              \
-                                  (fa::lds_char*)v0, (fa::lds_char*)v1);               \
-  }
-
-FA_FWD_FP8_WIDE_KERNEL(fa_fwd_fp8_d256_nomask, false)
-FA_FWD_FP8_WIDE_KERNEL(fa_fwd_fp8_d256_causal, true)
 
 namespace fa {
 
-int fwd_fp8_rows_per_block(int d) { return d == 256 ? F8Wide::BM : 32 * 8; }
+// Waves per workgroup: eight (two per SIMD) at d = 64 and 128, four (one
+// per SIMD) at d = 256.
+static int fwd_fp8_waves(int d) { return d == 256 ? 4 : 8; }
+
+int fwd_fp8_rows_per_block(int d) { return 32 * fwd_fp8_waves(d); }
 
 const char* fwd_fp8_kernel_name(int d, bool causal) {
   switch (d) {
@@ -885,7 +544,7 @@ hipError_t launch_fwd_fp8(const FwdF8Params& p, int d, bool causal, hipStream_t 
   const dim3 grid((unsigned)(((p.Nq + bm - 1) / bm) * p.B * p.Hq));
   FwdF8Params arg = p;
   void* args[] = {&arg};
-  return hipLaunchKernel(fn, grid, dim3(64 * 8), args, 0, s);
+  return hipLaunchKernel(fn, grid, dim3(64 * fwd_fp8_waves(d)), args, 0, s);
 }
 
 }  // namespace fa
