@@ -71,7 +71,7 @@ ODD = [
     (1, 2, 2, 40, 120, 128, False),
     (1, 3, 1, 200, 130, 64, False),
     (1, 2, 1, 190, 190, 128, True),
-    # d = 256 (16 rows per wave, 128-key tiles): tails, GQA, Nq < Nk, one
+    # d = 256 (four waves of 32 rows, one per SIMD): tails, GQA, Nq < Nk, one
     # valid row in the last query block, head-major non-causal order
     (1, 2, 1, 200, 200, 256, False),
     (1, 2, 1, 200, 200, 256, True),
