@@ -27,15 +27,16 @@
 // order that the P^T registers hold.  O = v_factor * acc / l (bf16), LSE in
 // natural log of the scaled scores.
 //
-// Schedule: 32 query rows per wave, one 64-key tile per step; eight waves
-// per workgroup (two per SIMD) at d = 64 and 128, four (one per SIMD) at
-// d = 256, where O^T alone takes 128 registers.  The P V product of a tile
-// runs one step after its probabilities.  Two waves that share a SIMD issue
-// each step's MFMAs and its exponentials in opposite orders, so one wave's
-// softmax overlaps the other wave's products; a wave alone on its SIMD
-// (d = 256) leaves both halves to the compiler, which interleaves them.  K
-// and V tiles are copied two steps ahead into three LDS buffers each, so
-// the per-step barrier rarely waits for memory.
+// Schedule: 32 query rows per wave, one 64-key tile per step.  The P V
+// product of a tile runs one step after its probabilities, so a step's
+// MFMAs do not depend on its exponentials.  At d = 128 eight waves share a
+// workgroup (two per SIMD), and the two waves of a SIMD issue the MFMAs and
+// the exponentials in opposite orders, so one wave's softmax overlaps the
+// other wave's products.  At d = 64 and 256 a workgroup has four waves and
+// the compiler interleaves each wave's MFMAs with its own exponentials; at
+// d = 64 three workgroups share a CU, at d = 256 (O^T alone takes 128
+// registers) one.  K and V tiles are copied two steps ahead into three LDS
+// buffers each, so the per-step barrier rarely waits for memory.
 
 #include "fa_internal.h"
 
@@ -320,10 +321,13 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
   // and w+4 of the workgroup) take the two halves in opposite orders (wave
   // group G = 1: products, then probabilities; G = 0: probabilities, then
   // products), so that one wave's exponentials run while the other wave's
-  // MFMAs do.  A scheduling barrier keeps each order as written.  With four
-  // waves (d = 256) each wave has its SIMD to itself: both halves then form
-  // one scheduling region and the compiler interleaves the wave's MFMAs with
-  // its own exponentials (+14% to +15% over the fixed order at d = 256).
+  // MFMAs do.  A scheduling barrier keeps each order as written.  In a
+  // four-wave workgroup (d = 64 and 256) no wave of the same workgroup
+  // shares the SIMD: both halves then form one scheduling region and the
+  // compiler interleaves the wave's MFMAs with its own exponentials (+14% to
+  // +15% over the fixed order at d = 256; at d = 64, +16% to +20% over eight
+  // waves in the two orders, while at d = 128 the eight-wave order measured
+  // 1% faster at the long prefill and the d = 128 sweep shape).
   //
   // Buffers: K_{j+1} and V_{j-1} are read here; K_{j+3} is loaded over K_j
   // (read in the previous step) and V_{j+1} over V_{j-2}.  Every copy is
@@ -494,7 +498,7 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
 }  // namespace fa
 
 #define FA_FWD_FP8_KERNEL(NAME, D, NW, CAUSAL)                                          \
-  extern "C" __global__ void __launch_bounds__(64 * NW, NW / 4) NAME(fa::FwdF8Params p) { \
+  extern "C" __global__ void __launch_bounds__(64 * NW, D == 256 ? 1 : 2) NAME(fa::FwdF8Params p) { \
     using Sh = fa::F8Shape<D, NW>;                                                     \
     __shared__ __attribute__((aligned(1024))) char k0[Sh::TILE];                       \
     __shared__ __attribute__((aligned(1024))) char k1[Sh::TILE];                       \
@@ -507,8 +511,8 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
                                     (fa::lds_char*)v1, (fa::lds_char*)v2);             \
   }
 
-FA_FWD_FP8_KERNEL(fa_fwd_fp8_d64_nomask, 64, 8, false)
-FA_FWD_FP8_KERNEL(fa_fwd_fp8_d64_causal, 64, 8, true)
+FA_FWD_FP8_KERNEL(fa_fwd_fp8_d64_nomask, 64, 4, false)
+FA_FWD_FP8_KERNEL(fa_fwd_fp8_d64_causal, 64, 4, true)
 FA_FWD_FP8_KERNEL(fa_fwd_fp8_d128_nomask, 128, 8, false)
 FA_FWD_FP8_KERNEL(fa_fwd_fp8_d128_causal, 128, 8, true)
 FA_FWD_FP8_KERNEL(fa_fwd_fp8_d256_nomask, 256, 4, false)
@@ -517,9 +521,9 @@ FA_FWD_FP8_KERNEL(fa_fwd_fp8_d256_causal, 256, 4, true)
 
 namespace fa {
 
-// Waves per workgroup: eight (two per SIMD) at d = 64 and 128, four (one
-// per SIMD) at d = 256.
-static int fwd_fp8_waves(int d) { return d == 256 ? 4 : 8; }
+// Waves per workgroup: eight (two per SIMD) at d = 128, four at d = 64
+// (three workgroups per CU) and d = 256 (one).
+static int fwd_fp8_waves(int d) { return d == 128 ? 8 : 4; }
 
 int fwd_fp8_rows_per_block(int d) { return 32 * fwd_fp8_waves(d); }
 
