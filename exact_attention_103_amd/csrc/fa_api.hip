@@ -224,7 +224,7 @@ int fa_fwd_fp8_devscale(const void* q, const void* k, const void* v, void* o, fl
 }
 
 size_t fa_fp8_quantize_workspace_size(int rows, int d) {
-  if (rows <= 0 || (d != 64 && d != 128)) return 0;
+  if (rows <= 0 || (d != 64 && d != 128 && d != 256)) return 0;
   return 4 * (size_t)fa::quant_blocks(rows, d);
 }
 
@@ -232,7 +232,7 @@ int fa_fp8_quantize(const void* x, void* codes, float* descale, const void* sign
                     int d, void* workspace, size_t workspace_bytes, void* stream) {
   if (!x || !codes || !descale) return FA_ERR_NULL;
   if (rows <= 0) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_HEAD_DIM;
   if (!aligned16(x) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(descale) & 3u) != 0)
     return FA_ERR_ALIGN;
   const int64_t x_bytes = checked_product({rows, d, 2});

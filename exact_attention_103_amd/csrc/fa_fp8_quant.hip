@@ -35,9 +35,11 @@
 // transform's four low index bits are butterflies inside a lane (one add or
 // subtract per element each), the others butterflies between lanes j and
 // j ^ m, exchanged with DPP moves inside the 16-lane rows of the wave (a row
-// of d = 128 is half a DPP row).  Sixteen elements per lane keep one more
-// stage inside the lane than eight would, and drop the lane distance 8,
-// whose exchange takes two DPP moves.
+// of d = 64 is a quarter of a DPP row, of d = 128 half of one, of d = 256 a
+// whole one, where distance 8 is the row rotation by 8 lanes).  Sixteen
+// elements per lane keep one more stage inside the lane than eight would.
+// With rotation, d = 128 moves its three high bits into the lanes through
+// an LDS transpose instead (below).
 
 #include "fa_internal.h"
 
@@ -56,7 +58,7 @@ struct QShape {
   static constexpr int L = D / 16;          // lanes per row
   static constexpr int RPW = 64 / L;        // rows per wave
   static constexpr int RPB = RPW * (kQuantThreads / 64);   // rows per workgroup pass
-  static_assert(D == 64 || D == 128, "rotation head dims");
+  static_assert(D == 64 || D == 128 || D == 256, "rotation head dims");
 };
 
 // Sign-bit masks of this lane's 16 elements (0 without rotation).
@@ -67,7 +69,8 @@ __device__ __forceinline__ void sign_masks(const int8_t* signs, int j, unsigned 
 
 // x from lane i ^ M within the 16-lane DPP row, as VALU moves (no LDS):
 // M = 1, 2 are quad permutations; M = 4 is the quad permutation i ^ 3
-// followed by the half-row mirror (i ^ 7).
+// followed by the half-row mirror (i ^ 7); M = 8 is the row rotation by 8
+// lanes (i + 8 mod 16 = i ^ 8).
 template <int M>
 __device__ __forceinline__ float lane_xor(float x) {
   const int v = __float_as_int(x);
@@ -78,10 +81,13 @@ __device__ __forceinline__ float lane_xor(float x) {
     r = __builtin_amdgcn_mov_dpp(v, kQuadXor1, 0xF, 0xF, true);
   } else if constexpr (M == 2) {
     r = __builtin_amdgcn_mov_dpp(v, kQuadXor2, 0xF, 0xF, true);
-  } else {
-    static_assert(M == 4, "lane distance within an 8-lane group");
+  } else if constexpr (M == 4) {
     r = __builtin_amdgcn_mov_dpp(v, kQuadXor3, 0xF, 0xF, true);
     r = __builtin_amdgcn_mov_dpp(r, kHalfMirror, 0xF, 0xF, true);
+  } else {
+    static_assert(M == 8, "lane distance within a 16-lane row");
+    constexpr int kRowRotate8 = 0x128;
+    r = __builtin_amdgcn_mov_dpp(v, kRowRotate8, 0xF, 0xF, true);
   }
   return __int_as_float(r);
 }
@@ -138,8 +144,9 @@ __device__ __forceinline__ void inlane_butterflies(float (&v)[16]) {
 }
 
 // The lane's 16 values as fp32 and, when `rotate`, with the signs applied
-// and the Walsh-Hadamard transform of the row (d = 64: index bits 0..3 in
-// the lane, bits 4..5 between lanes through DPP moves).
+// and the Walsh-Hadamard transform of the row: index bits 0..3 in the lane,
+// the higher bits (two at d = 64, four at d = 256; d = 128 takes this path
+// only without rotation) between the row's lanes through DPP moves.
 template <int D>
 __device__ __forceinline__ void transform(Row16 w, const unsigned (&neg)[16], bool rotate, int j,
                                           float (&v)[16]) {
@@ -148,7 +155,8 @@ __device__ __forceinline__ void transform(Row16 w, const unsigned (&neg)[16], bo
   inlane_butterflies<15>(v);
   lane_butterfly<1>(v, j);
   lane_butterfly<2>(v, j);
-  if constexpr (QShape<D>::L == 8) lane_butterfly<4>(v, j);
+  if constexpr (QShape<D>::L >= 8) lane_butterfly<4>(v, j);
+  if constexpr (QShape<D>::L >= 16) lane_butterfly<8>(v, j);
 }
 
 // d = 128 with rotation: the transform runs entirely inside lanes, with one
@@ -378,6 +386,7 @@ __device__ __forceinline__ void quant_body(const QuantParams& p) {
 
 FA_FP8_QUANT_KERNELS(64)
 FA_FP8_QUANT_KERNELS(128)
+FA_FP8_QUANT_KERNELS(256)
 
 namespace fa {
 
@@ -390,12 +399,18 @@ int quant_blocks(int rows, int d) {
 const char* quant_kernel_name(int d, int stage) {
   if (d == 64) return stage == 0 ? "fa_fp8_absmax_d64" : "fa_fp8_quant_d64";
   if (d == 128) return stage == 0 ? "fa_fp8_absmax_d128" : "fa_fp8_quant_d128";
+  if (d == 256) return stage == 0 ? "fa_fp8_absmax_d256" : "fa_fp8_quant_d256";
   return nullptr;
 }
 
 hipError_t launch_quant(const QuantParams& p, int d, hipStream_t s) {
-  const void* k0 = d == 64 ? (const void*)fa_fp8_absmax_d64 : (const void*)fa_fp8_absmax_d128;
-  const void* k1 = d == 64 ? (const void*)fa_fp8_quant_d64 : (const void*)fa_fp8_quant_d128;
+  const void *k0, *k1;
+  switch (d) {
+    case 64: k0 = (const void*)fa_fp8_absmax_d64; k1 = (const void*)fa_fp8_quant_d64; break;
+    case 128: k0 = (const void*)fa_fp8_absmax_d128; k1 = (const void*)fa_fp8_quant_d128; break;
+    case 256: k0 = (const void*)fa_fp8_absmax_d256; k1 = (const void*)fa_fp8_quant_d256; break;
+    default: return hipErrorInvalidValue;
+  }
   QuantParams arg = p;
   void* args[] = {&arg};
   hipError_t e = hipLaunchKernel(k0, dim3(p.nblocks), dim3(kQuantThreads), args, 0, s);

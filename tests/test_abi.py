@@ -355,10 +355,11 @@ def test_fp8_rejects(kw, code):
 def test_quantize_names_and_workspace():
     assert fa.fa_fp8_quantize_kernel_name(128, 0) == "fa_fp8_absmax_d128"
     assert fa.fa_fp8_quantize_kernel_name(64, 1) == "fa_fp8_quant_d64"
+    assert fa.fa_fp8_quantize_kernel_name(256, 0) == "fa_fp8_absmax_d256"
     assert fa.fa_fp8_quantize_kernel_name(32, 0) is None
     assert fa.fa_fp8_quantize_kernel_name(128, 2) is None
-    # One float per workgroup of the first pass: 32 rows (d = 128) or 64
-    # rows (d = 64) per workgroup, at most 1024 workgroups.
+    # One float per workgroup of the first pass: 64 rows (d = 64), 32
+    # (d = 128) or 16 (d = 256) per workgroup, at most 1024 workgroups.
     assert fa.fa_fp8_quantize_workspace_size(1, 128) == 4
     assert fa.fa_fp8_quantize_workspace_size(32, 128) == 4
     assert fa.fa_fp8_quantize_workspace_size(33, 128) == 8
@@ -366,7 +367,9 @@ def test_quantize_names_and_workspace():
     assert fa.fa_fp8_quantize_workspace_size(65, 64) == 8
     assert fa.fa_fp8_quantize_workspace_size(32 * 16384, 128) == 4096
     assert fa.fa_fp8_quantize_workspace_size(0, 128) == 0
-    assert fa.fa_fp8_quantize_workspace_size(16, 256) == 0
+    assert fa.fa_fp8_quantize_workspace_size(16, 256) == 4
+    assert fa.fa_fp8_quantize_workspace_size(17, 256) == 8
+    assert fa.fa_fp8_quantize_workspace_size(16, 512) == 0
 
 
 S8 = 0x700000   # placeholder address of the signs vector
@@ -376,7 +379,7 @@ DS = 0x800000   # placeholder address of the descale output
 @cpu_only
 @pytest.mark.parametrize("kw,code", [
     (dict(x=0), -1), (dict(codes=0), -1), (dict(ds=0), -1),
-    (dict(rows=0), -2), (dict(rows=-5), -2), (dict(d=32), -3), (dict(d=256), -3),
+    (dict(rows=0), -2), (dict(rows=-5), -2), (dict(d=32), -3), (dict(d=512), -3),
     (dict(x=Q + 8), -4), (dict(codes=O + 4), -4), (dict(ds=DS + 2), -4),
     (dict(ws=0), -5), (dict(wsb=4), -5), (dict(ws=W + 4), -4),
     (dict(codes=Q + 64), -9), (dict(ds=Q + 16), -9), (dict(ws=O), -9),

@@ -67,6 +67,10 @@ CASES = [  # (rows, d, rotated, outliers)
     # 8 rows: one wave's row group, the other waves idle; 50001 rows: the
     # grid's second row group per iteration ends partway.
     (8, 128, True, True), (50001, 128, True, False),
+    # d = 256: a whole DPP row per tensor row (lane distance 8 is the row
+    # rotation); 5 rows: part of one wave's row group
+    (5, 256, True, False), (1000, 256, True, True), (3001, 256, False, False),
+    (20000, 256, True, False),
 ]
 
 
@@ -148,7 +152,8 @@ def _oracle_pipeline(qb, kb, vb, signs, causal, scale):
 
 
 E2E = [(1, 4, 2, 200, 200, 128, True), (1, 2, 2, 130, 300, 64, False),
-       (2, 4, 4, 257, 257, 128, False), (1, 8, 2, 64, 1000, 128, True)]
+       (2, 4, 4, 257, 257, 128, False), (1, 8, 2, 64, 1000, 128, True),
+       (1, 2, 1, 200, 200, 256, True), (1, 4, 2, 130, 300, 256, False)]
 
 
 @pytest.mark.parametrize("shape", E2E, ids=[
