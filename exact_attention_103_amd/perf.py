@@ -114,7 +114,7 @@ def main():
                           "pct_of_5000": round(100 * flop / ms / 1e9 / 5000, 1)}), flush=True)
         del q8, k8, v8, o, lse
     for name, B, H, N, d in (("long", 1, 32, 16384, 128), ("train", 8, 16, 2048, 128),
-                             ("sweep_d64", 2, 16, 4096, 64)):
+                             ("sweep_d64", 2, 16, 4096, 64), ("sweep_d256", 2, 16, 4096, 256)):
         # fp8 input step on one bf16 tensor: rotated (Q, K) and plain (V);
         # GB/s over 3 bytes per element (bf16 read, e4m3 code written).
         x = torch.randn(B, H, N, d, device="cuda").to(torch.bfloat16)
