@@ -452,10 +452,8 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
     // products keeps a single S^T tile live.
     if constexpr (kPipe) s_tile(kr, sn);
 
-    // At d = 256, LLVM's instruction group strategy 0 (LDS reads interleaved
-    // with the MFMAs) schedules this section; the 8-wave d = 128 tile has an
-    // explicit schedule (below).
-    if constexpr (D == 256) __builtin_amdgcn_iglp_opt(0);
+    // The 8-wave d = 128 tile has an explicit schedule for this section
+    // (below); d = 256 runs fwd_body_late.
     // Per 16-key chunk kc: probabilities P = 2^(S*c - m) become the bf16 B
     // operand (registers 8*(kc%2).. of block kc/2), then O^T += V^T P^T for
     // every d block, the V^T operand coming from two transposing reads and
@@ -565,6 +563,261 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
   }
 }
 
+// d = 256 forward with the P V product one tile late (the step schedule of
+// the fp8 kernel): four waves of 32 rows, one per SIMD (O^T alone takes 128
+// registers), 32-key tiles.  Step j issues S^T of tile j+1 and P V of tile
+// j-1 on the MFMA pipe and turns tile j's scores into bf16 probabilities on
+// the VALU; neither half waits for the other, so the wave, alone on its
+// SIMD, interleaves them (LLVM's instruction-group strategy 0 over the
+// step: +12% over the same step without it and over the in-step P V body
+// above).  K is copied three tiles ahead and V one, into three LDS buffers
+// each, so every copy has two steps before its tile is read and the step
+// barrier waits only for the previous step's copies.  The rescale rule, the
+// masking and the arithmetic per accumulator are those of fwd_body: both
+// give the same bits.
+template <int D, int BN, bool CAUSAL>
+__device__ __forceinline__ void fwd_body_late(const FwdParams& p, lds_char* kb0, lds_char* kb1,
+                                              lds_char* kb2, lds_char* vb0, lds_char* vb1,
+                                              lds_char* vb2) {
+  constexpr int NW = 4;
+  using S = FwdShape<D, BN, NW, 1>;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int hl = lane >> 5;
+  const int n = lane & 31;
+
+  const int BH = p.B * p.Hq;
+  const int nqb = (p.Nq + S::BM - 1) / S::BM;
+  // Query block major, heaviest causal blocks first (as fwd_body).
+  const int bh = blockIdx.x % BH;
+  const int qi = blockIdx.x / BH;
+  const int qblk = CAUSAL ? (nqb - 1 - qi) : qi;
+  const int b = bh / p.Hq;
+  const int h = bh - b * p.Hq;
+  const int g = h / p.group;
+  const int q0 = qblk * S::BM;
+  const int qw = q0 + 32 * wave;
+  const int off = p.Nk - p.Nq;
+  const int row = qw + n;
+
+  const uint16_t* qbase = p.q + (size_t)(b * p.Hq + h) * p.Nq * D;
+  const uint16_t* kbase = p.k + (size_t)(b * p.Hkv + g) * p.Nk * D;
+  const uint16_t* vbase = p.v + (size_t)(b * p.Hkv + g) * p.Nk * D;
+
+  int nkt = (p.Nk + BN - 1) / BN;
+  if (CAUSAL) nkt = min(nkt, (min(q0 + S::BM, p.Nq) - 1 + off) / BN + 1);
+  auto k_rsrc = [&](int t) {
+    return tile_rsrc<D>(kbase + (size_t)t * BN * D, t < nkt ? min(p.Nk - t * BN, BN) : 0);
+  };
+  auto v_rsrc = [&](int t) {
+    return tile_rsrc<D>(vbase + (size_t)t * BN * D, t < nkt ? min(p.Nk - t * BN, BN) : 0);
+  };
+  int kvo[S::KLOADS];
+#pragma unroll
+  for (int i = 0; i < S::KLOADS; ++i) kvo[i] = k_load_voff<D, BN, NW>(wave, lane, i);
+  __amdgpu_buffer_rsrc_t no_rows = tile_rsrc<D>(kbase, 0);
+  const int vvo0 = v_load_voff<D, BN, NW>(wave, lane, 0);
+  const int vvo1 = VParity<D, BN, NW>::value ? v_load_voff<D, BN, NW>(wave, lane, 1) : vvo0;
+
+  // The V buffers start as zeros: a copy through a resource of fewer rows
+  // leaves the LDS rows past them as they were, and those rows meet
+  // probability 0 in the P V product, which stays 0 only for finite values.
+  {
+    using v4 = unsigned __attribute__((ext_vector_type(4)));
+    constexpr int per = S::TILE / 16 / S::NT;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      *(__attribute__((address_space(3))) v4*)(vb0 + (i * S::NT + tid) * 16) = v4{};
+      *(__attribute__((address_space(3))) v4*)(vb1 + (i * S::NT + tid) * 16) = v4{};
+      *(__attribute__((address_space(3))) v4*)(vb2 + (i * S::NT + tid) * 16) = v4{};
+    }
+    __syncthreads();
+  }
+
+  bf16x8 qf[S::KSTEPS];
+#pragma unroll
+  for (int t = 0; t < S::KSTEPS; ++t)
+    qf[t] = row < p.Nq ? *reinterpret_cast<const bf16x8*>(qbase + (size_t)row * D + 16 * t + 8 * hl)
+                       : bf16x8{};
+
+  const int koff = n * S::KRB + hl * 16;
+  const int j16 = lane & 15;
+  const int vrow = 4 * hl + (j16 >> 2);
+  const int vx = v_xor<S::RB>(vrow) >> 2;
+  const int voff = vrow * S::RB + 32 * ((lane >> 4) & 1) + 16 * ((j16 & 3) >> 1) + 8 * (j16 & 1);
+  int vaddr[S::DB];
+#pragma unroll
+  for (int db = 0; db < S::DB; ++db) vaddr[db] = voff + 64 * (db ^ vx);
+
+  f32x16 oacc[S::DB];
+#pragma unroll
+  for (int db = 0; db < S::DB; ++db) oacc[db] = f32x16{};
+  float m_run = -1e30f;
+  float l_run[2] = {0.f, 0.f};
+
+  auto s_tile = [&](const lds_char* kt, f32x16 (&sacc)[S::KB]) {
+#pragma unroll
+    for (int kb = 0; kb < S::KB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < S::KSTEPS; ++t) {
+#pragma unroll
+      for (int kb = 0; kb < S::KB; ++kb) {
+        const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(
+            kt + koff + 32 * t + 32 * kb * S::KRB);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], sacc[kb], 0, 0, 0);
+      }
+    }
+  };
+  auto pv = [&](const lds_char* vt, const bf16x8 (&pbt)[S::KC]) {
+#pragma unroll
+    for (int kc = 0; kc < S::KC; ++kc) {
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db) {
+        const lds_char* va = vt + vaddr[db] + 16 * kc * S::RB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(va));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(va + 8 * S::RB));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pbt[kc], oacc[db], 0, 0, 0);
+      }
+    }
+  };
+  auto needs_mask = [&](int t) {
+    const int t0 = t * BN;
+    return (t0 + BN > p.Nk) || (CAUSAL && t0 + BN - 1 > qw + off);
+  };
+  auto mask_tile = [&](f32x16 (&sacc)[S::KB], int t) {
+    const int lim = (CAUSAL ? min(p.Nk - 1, row + off) : p.Nk - 1) - t * BN - 4 * hl;
+#pragma unroll
+    for (int kb = 0; kb < S::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
+  };
+  auto tile_max = [&](const f32x16 (&sacc)[S::KB]) {
+    float x = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < S::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) x = fmaxf(fmaxf(x, sacc[kb][r]), sacc[kb][r + 1]);
+    return half_max(x) * p.c;
+  };
+
+  bf16x8 pbp[S::KC];
+#pragma unroll
+  for (int kc = 0; kc < S::KC; ++kc) pbp[kc] = bf16x8{};
+  auto step = [&](const lds_char* kr, const lds_char* vprev, lds_char* kw, lds_char* vw,
+                  f32x16 (&sc)[S::KB], f32x16 (&sn)[S::KB], int j) {
+    FA_STAGE_FENCE();
+    load_k<D, BN, NW>(k_rsrc(j + 3), no_rows, kw, wave, kvo);
+    load_v<D, BN, NW>(v_rsrc(j + 1), vw, wave, vvo0, vvo1);
+    FA_STAGE_FENCE();
+
+    bf16x8 pbc[S::KC];
+    float alpha = 1.f;
+    bool moved = false;
+    auto probs = [&]() {
+      if (needs_mask(j)) mask_tile(sc, j);
+      const float m_new = fmaxf(m_run, tile_max(sc));
+      moved = __any(m_new > m_run + kRescaleThreshold);
+      if (moved) {
+        alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run[0] *= alpha;
+        l_run[1] *= alpha;
+        m_run = m_new;
+      }
+      const float nm = -m_run;
+#pragma unroll
+      for (int kc = 0; kc < S::KC; ++kc) {
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[kc >> 1][8 * (kc & 1) + i], p.c, nm));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[kc >> 1][8 * (kc & 1) + i + 1], p.c, nm));
+          l_run[0] += e0;
+          l_run[1] += e1;
+          pbc[kc][i] = (__bf16)e0;
+          pbc[kc][i + 1] = (__bf16)e1;
+        }
+      }
+    };
+    auto products = [&]() {
+      s_tile(kr, sn);
+      if (j > 0) pv(vprev, pbp);
+    };
+    __builtin_amdgcn_iglp_opt(0);
+    products();
+    probs();
+    // The accumulator holds tiles up to j-1 against the old reference.
+    if (moved) {
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+#pragma unroll
+    for (int kc = 0; kc < S::KC; ++kc) pbp[kc] = pbc[kc];
+    // Only this step's copies (a K and a V tile) may stay in flight.
+    copies_in_flight_barrier<S::KLOADS + S::LOADS>();
+  };
+
+  f32x16 sa[S::KB], sb[S::KB];
+  load_k<D, BN, NW>(k_rsrc(0), no_rows, kb0, wave, kvo);
+  load_v<D, BN, NW>(v_rsrc(0), vb0, wave, vvo0, vvo1);
+  load_k<D, BN, NW>(k_rsrc(1), no_rows, kb1, wave, kvo);
+  load_k<D, BN, NW>(k_rsrc(2), no_rows, kb2, wave, kvo);
+  __syncthreads();
+  s_tile(kb0, sa);
+  __syncthreads();
+  lds_char* const kbs[3] = {kb0, kb1, kb2};
+  lds_char* const vbs[3] = {vb0, vb1, vb2};
+  // Tile t lives in K and V buffer t % 3; six steps per iteration keep the
+  // buffers and the S^T register set (which alternates) compile-time
+  // constants.
+  for (int j0 = 0; j0 < nkt; j0 += 6) {
+    static_for<0, 6>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      const int j = j0 + u;
+      if (u == 0 || j < nkt) {
+        auto& sc = (u % 2 == 0) ? sa : sb;
+        auto& sn = (u % 2 == 0) ? sb : sa;
+        step(kbs[(u + 1) % 3], vbs[(u + 2) % 3], kbs[u % 3], vbs[(u + 1) % 3], sc, sn, j);
+      }
+    });
+  }
+  // No copy into this workgroup's LDS may still be in flight past here.
+  __builtin_amdgcn_s_waitcnt(0);
+  // P V of the last tile, with the whole wave active: the empty asm
+  // statements use the accumulators, which keeps the compiler from sinking
+  // the products into the row-predicated store below.
+  {
+    const int last = nkt - 1;
+    const lds_char* vl = last % 3 == 0 ? vb0 : last % 3 == 1 ? vb1 : vb2;
+    pv(vl, pbp);
+  }
+#pragma unroll
+  for (int db = 0; db < S::DB; ++db) asm volatile("" : "+v"(oacc[db]));
+
+  const float l_tot = half_sum(l_run[0] + l_run[1]);
+  if (row < p.Nq) {
+    const float inv = 1.0f / l_tot;
+    uint16_t* orow = p.o + ((size_t)(b * p.Hq + h) * p.Nq + row) * D;
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x2 lo = {(__bf16)(oacc[db][4 * r4 + 0] * inv), (__bf16)(oacc[db][4 * r4 + 1] * inv)};
+        bf16x2 hi = {(__bf16)(oacc[db][4 * r4 + 2] * inv), (__bf16)(oacc[db][4 * r4 + 3] * inv)};
+        uint2 w;
+        w.x = __builtin_bit_cast(unsigned, lo);
+        w.y = __builtin_bit_cast(unsigned, hi);
+        *reinterpret_cast<uint2*>(orow + 32 * db + 8 * r4 + 4 * hl) = w;
+      }
+    if (hl == 0) p.lse[(size_t)(b * p.Hq + h) * p.Nq + row] = (m_run + log2f(l_tot)) * kLn2;
+  }
+}
+
 }  // namespace
 }  // namespace fa
 
@@ -582,6 +835,21 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, lds_char* kb0, lds_
         (fa::lds_char*)k1, (fa::lds_char*)v0, (fa::lds_char*)v1);                     \
   }
 
+// d = 256: the body with P V one tile late (fwd_body_late), one wave per
+// SIMD, three K and three V buffers.
+#define FA_FWD_KERNEL_LATE(NAME, D, BN, CAUSAL)                                       \
+  extern "C" __global__ void __launch_bounds__(256, 1) NAME(fa::FwdParams p) {        \
+    using Sh = fa::FwdShape<D, BN, 4, 1>;                                             \
+    __shared__ __attribute__((aligned(1024))) char k0[Sh::KTILE];                     \
+    __shared__ __attribute__((aligned(1024))) char k1[Sh::KTILE];                     \
+    __shared__ __attribute__((aligned(1024))) char k2[Sh::KTILE];                     \
+    __shared__ __attribute__((aligned(1024))) char v0[Sh::TILE];                      \
+    __shared__ __attribute__((aligned(1024))) char v1[Sh::TILE];                      \
+    __shared__ __attribute__((aligned(1024))) char v2[Sh::TILE];                      \
+    fa::fwd_body_late<D, BN, CAUSAL>(p, (fa::lds_char*)k0, (fa::lds_char*)k1,          \
+        (fa::lds_char*)k2, (fa::lds_char*)v0, (fa::lds_char*)v1, (fa::lds_char*)v2);  \
+  }
+
 // Tile table (head dim: keys per tile, waves, query blocks of 32 rows per
 // wave, waves per SIMD, causal idle-tile skip, head-major XCD order).  It
 // must match fwd_tile() below.  d = 128 has a 256-row tile (8 waves share
@@ -597,8 +865,8 @@ FA_FWD_KERNEL(fa_fwd_d128_nomask, 128, 64, 8, 1, false, 2, false, true)
 FA_FWD_KERNEL(fa_fwd_d128_causal, 128, 64, 8, 1, true, 2, true, true)
 FA_FWD_KERNEL(fa_fwd_d128_nomask_bm128, 128, 64, 4, 1, false, 2, false, false)
 FA_FWD_KERNEL(fa_fwd_d128_causal_bm128, 128, 64, 4, 1, true, 2, true, false)
-FA_FWD_KERNEL(fa_fwd_d256_nomask, 256, 32, 4, 1, false, 1, false, false)
-FA_FWD_KERNEL(fa_fwd_d256_causal, 256, 32, 4, 1, true, 1, false, false)
+FA_FWD_KERNEL_LATE(fa_fwd_d256_nomask, 256, 32, false)
+FA_FWD_KERNEL_LATE(fa_fwd_d256_causal, 256, 32, true)
 
 namespace fa {
 namespace {
