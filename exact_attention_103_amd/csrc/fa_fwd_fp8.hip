@@ -324,7 +324,8 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
   // MFMAs do.  A scheduling barrier keeps each order as written.  In a
   // four-wave workgroup (d = 64 and 256) no wave of the same workgroup
   // shares the SIMD: both halves then form one scheduling region and the
-  // compiler interleaves the wave's MFMAs with its own exponentials (+14% to
+  // compiler interleaves the wave's MFMAs with its own exponentials, under
+  // LLVM's instruction-group strategy 0 (+1% to +2% over its default; +14% to
   // +15% over the fixed order at d = 256; at d = 64, +16% to +20% over eight
   // waves in the two orders, while at d = 128 the eight-wave order measured
   // 1% faster at the long prefill and the d = 128 sweep shape).
@@ -377,6 +378,7 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
       if (j > 0) pv(vprev, pf);
     };
     if constexpr (NW == 4) {
+      __builtin_amdgcn_iglp_opt(0);
       products();
       probs();
     } else if constexpr (decltype(group)::value) {
