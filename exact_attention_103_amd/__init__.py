@@ -476,7 +476,7 @@ def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal=False, scale=None, 
 
 def fp8_quantize(x, signs=None, codes=None, descale=None, workspace=None):
     """Incoherent processing and per-tensor e4m3 quantisation of a bf16
-    device tensor [..., d] (d = 64, 128 or 256): rotated by diag(signs) H_d /
+    device tensor [..., d] (d = 32, 64, 128 or 256): rotated by diag(signs) H_d /
     sqrt(d) when `signs` (int8 device tensor [d], negative = -1) is given.
     Returns (codes uint8 tensor of x's shape, descale float32 device tensor
     [1]) with codes * descale approximating the rotated x."""

@@ -68,7 +68,7 @@ int fwd_fp8_common(const void* q, const void* k, const void* v, void* o, float* 
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
   if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
   if (causal && Nq > Nk) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128 && d != 256) return FA_ERR_HEAD_DIM;
+  if (!supported_d(d)) return FA_ERR_HEAD_DIM;
   if (!scale_ok(scale)) return FA_ERR_SCALE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_ALIGN;
@@ -224,7 +224,7 @@ int fa_fwd_fp8_devscale(const void* q, const void* k, const void* v, void* o, fl
 }
 
 size_t fa_fp8_quantize_workspace_size(int rows, int d) {
-  if (rows <= 0 || (d != 64 && d != 128 && d != 256)) return 0;
+  if (rows <= 0 || !supported_d(d)) return 0;
   return 4 * (size_t)fa::quant_blocks(rows, d);
 }
 
@@ -232,7 +232,7 @@ int fa_fp8_quantize(const void* x, void* codes, float* descale, const void* sign
                     int d, void* workspace, size_t workspace_bytes, void* stream) {
   if (!x || !codes || !descale) return FA_ERR_NULL;
   if (rows <= 0) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128 && d != 256) return FA_ERR_HEAD_DIM;
+  if (!supported_d(d)) return FA_ERR_HEAD_DIM;
   if (!aligned16(x) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(descale) & 3u) != 0)
     return FA_ERR_ALIGN;
   const int64_t x_bytes = checked_product({rows, d, 2});
@@ -498,7 +498,7 @@ const char* fa_strerror(int status) {
     case FA_OK: return "success";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid shape (sizes must be > 0, Hq a multiple of Hkv, causal needs Nq <= Nk)";
-    case FA_ERR_HEAD_DIM: return "unsupported head dimension (32, 64, 128 or 256; fp8 forward: 64, 128 or 256)";
+    case FA_ERR_HEAD_DIM: return "unsupported head dimension (32, 64, 128 or 256)";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case FA_ERR_WORKSPACE: return "workspace is NULL or too small";
     case FA_ERR_SPLITS: return "num_splits out of range";

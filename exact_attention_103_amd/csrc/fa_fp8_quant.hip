@@ -35,8 +35,9 @@
 // transform's four low index bits are butterflies inside a lane (one add or
 // subtract per element each), the others butterflies between lanes j and
 // j ^ m, exchanged with DPP moves inside the 16-lane rows of the wave (a row
-// of d = 64 is a quarter of a DPP row, of d = 128 half of one, of d = 256 a
-// whole one, where distance 8 is the row rotation by 8 lanes).  Sixteen
+// of d = 32 is an eighth of a DPP row, of d = 64 a quarter, of d = 128 half
+// of one, of d = 256 a whole one, where distance 8 is the row rotation by 8
+// lanes).  Sixteen
 // elements per lane keep one more stage inside the lane than eight would.
 // With rotation, d = 128 moves its three high bits into the lanes through
 // an LDS transpose instead (below).
@@ -58,7 +59,7 @@ struct QShape {
   static constexpr int L = D / 16;          // lanes per row
   static constexpr int RPW = 64 / L;        // rows per wave
   static constexpr int RPB = RPW * (kQuantThreads / 64);   // rows per workgroup pass
-  static_assert(D == 64 || D == 128 || D == 256, "rotation head dims");
+  static_assert(D == 32 || D == 64 || D == 128 || D == 256, "rotation head dims");
 };
 
 // Sign-bit masks of this lane's 16 elements (0 without rotation).
@@ -145,7 +146,7 @@ __device__ __forceinline__ void inlane_butterflies(float (&v)[16]) {
 
 // The lane's 16 values as fp32 and, when `rotate`, with the signs applied
 // and the Walsh-Hadamard transform of the row: index bits 0..3 in the lane,
-// the higher bits (two at d = 64, four at d = 256; d = 128 takes this path
+// the higher bits (one at d = 32, two at d = 64, four at d = 256; d = 128 takes this path
 // only without rotation) between the row's lanes through DPP moves.
 template <int D>
 __device__ __forceinline__ void transform(Row16 w, const unsigned (&neg)[16], bool rotate, int j,
@@ -154,7 +155,7 @@ __device__ __forceinline__ void transform(Row16 w, const unsigned (&neg)[16], bo
   if (!rotate) return;
   inlane_butterflies<15>(v);
   lane_butterfly<1>(v, j);
-  lane_butterfly<2>(v, j);
+  if constexpr (QShape<D>::L >= 4) lane_butterfly<2>(v, j);
   if constexpr (QShape<D>::L >= 8) lane_butterfly<4>(v, j);
   if constexpr (QShape<D>::L >= 16) lane_butterfly<8>(v, j);
 }
@@ -384,6 +385,7 @@ __device__ __forceinline__ void quant_body(const QuantParams& p) {
     fa::quant_body<D>(p);                                                                  \
   }
 
+FA_FP8_QUANT_KERNELS(32)
 FA_FP8_QUANT_KERNELS(64)
 FA_FP8_QUANT_KERNELS(128)
 FA_FP8_QUANT_KERNELS(256)
@@ -397,6 +399,7 @@ int quant_blocks(int rows, int d) {
 }
 
 const char* quant_kernel_name(int d, int stage) {
+  if (d == 32) return stage == 0 ? "fa_fp8_absmax_d32" : "fa_fp8_quant_d32";
   if (d == 64) return stage == 0 ? "fa_fp8_absmax_d64" : "fa_fp8_quant_d64";
   if (d == 128) return stage == 0 ? "fa_fp8_absmax_d128" : "fa_fp8_quant_d128";
   if (d == 256) return stage == 0 ? "fa_fp8_absmax_d256" : "fa_fp8_quant_d256";
@@ -406,6 +409,7 @@ const char* quant_kernel_name(int d, int stage) {
 hipError_t launch_quant(const QuantParams& p, int d, hipStream_t s) {
   const void *k0, *k1;
   switch (d) {
+    case 32: k0 = (const void*)fa_fp8_absmax_d32; k1 = (const void*)fa_fp8_quant_d32; break;
     case 64: k0 = (const void*)fa_fp8_absmax_d64; k1 = (const void*)fa_fp8_quant_d64; break;
     case 128: k0 = (const void*)fa_fp8_absmax_d128; k1 = (const void*)fa_fp8_quant_d128; break;
     case 256: k0 = (const void*)fa_fp8_absmax_d256; k1 = (const void*)fa_fp8_quant_d256; break;

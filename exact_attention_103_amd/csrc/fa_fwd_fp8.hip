@@ -66,13 +66,13 @@ struct F8Shape {
   static constexpr int BM = 32 * NW;       // query rows per workgroup
   static constexpr int RB = D;             // bytes per K or V row
   static constexpr int CPR = D / 16;       // 16-byte chunks per row
-  static constexpr int KSTEPS = D / 64;    // 32x32x64 k-steps over d
+  static constexpr int KSTEPS = D >= 64 ? D / 64 : 1;   // 32x32x64 k-steps over d
   static constexpr int KB = BN / 32;       // 32-key blocks per tile
   static constexpr int DB = D / 32;        // 32-row d blocks of O^T
   static constexpr int TILE = BN * RB;
   static constexpr int BLKS = TILE / 1024;
   static constexpr int LOADS = (BLKS + NW - 1) / NW;
-  static_assert(D % 64 == 0, "fp8 head dim");
+  static_assert(D == 32 || D % 64 == 0, "fp8 head dim");
 };
 
 // LDS tiles: 16-byte chunk c of row r at c ^ X(r).  Two read patterns meet
@@ -91,6 +91,10 @@ struct F8Shape {
 // 4.  All three touch every bank once per pass in either pattern (an
 // earlier X = i put two lanes on each bank of the V^T reads, and the
 // 128-byte rule on 256-byte rows two on each bank of the K reads).
+// 32-byte rows (eight per line, two chunks): X = (r / 8) mod 2 keeps the K
+// reads conflict-free; the V^T reads of rows {0..3} and {8..11} then share
+// their banks (two lanes per bank), which no chunk permutation inside a
+// 32-byte row can avoid.
 template <int RB>
 __device__ __forceinline__ int f8_xor(int r) {
   if constexpr (RB >= 256) {
@@ -98,8 +102,10 @@ __device__ __forceinline__ int f8_xor(int r) {
   } else if constexpr (RB == 128) {
     const int i = (r >> 1) & 7;
     return ((i & 1) << 1) | ((i >> 1) & 1) | (i & 4);
-  } else {
+  } else if constexpr (RB == 64) {
     return (r >> 2) & 3;
+  } else {
+    return (r >> 3) & 1;
   }
 }
 
@@ -219,11 +225,14 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
   if (CAUSAL) nkt = min(nkt, (min(q0 + S::BM, p.Nq) - 1 + off) / BN + 1);
 
   // Q^T B operand: lane (hl, n) holds Q[row][64t + 32hl .. +31].  Rows past
-  // Nq are zero.
+  // Nq are zero.  At d = 32 the one k-step's upper half (hl = 1) is zero,
+  // and those lanes' K operand repeats the row's 32 bytes: e4m3 has no
+  // infinity, so each added product is a zero unless the K row holds a NaN,
+  // which makes the score NaN in any case.
   v8i qf[S::KSTEPS];
 #pragma unroll
   for (int t = 0; t < S::KSTEPS; ++t) {
-    if (row < p.Nq) {
+    if (row < p.Nq && (D >= 64 || hl == 0)) {
       const uint8_t* src = p.q + ((size_t)bh * p.Nq + row) * D + 64 * t + 32 * hl;
       qf[t] = f8_mfma_operand(*reinterpret_cast<const v4i*>(src),
                               *reinterpret_cast<const v4i*>(src + 16));
@@ -232,8 +241,10 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
     }
   }
 
-  // K A-operand reads: row 32kb + n, chunks 4t + 2hl and +1.
+  // K A-operand reads: row 32kb + n, chunks 4t + 2hl and +1 (at d = 32
+  // chunks 0 and 1 for both lane halves).
   const int kx = f8_xor<S::RB>(n);
+  const int kc0 = D >= 64 ? 2 * hl : 0;
   // V^T A-operand reads (8-bit transposing loads): source lane s of a
   // 16-lane group (hl, g1) addresses key row vrow + 16u and 8 bytes at
   // column 32db + 16g1 + 8(s&1); lane i of the group then receives column
@@ -262,8 +273,8 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
 #pragma unroll
       for (int t = 0; t < S::KSTEPS; ++t) {
         const lds_char* rp = kt + (kb * 32 + n) * S::RB;
-        const v4i lo = *(const __attribute__((address_space(3))) v4i*)(rp + (((4 * t + 2 * hl) ^ kx) << 4));
-        const v4i hi = *(const __attribute__((address_space(3))) v4i*)(rp + (((4 * t + 2 * hl + 1) ^ kx) << 4));
+        const v4i lo = *(const __attribute__((address_space(3))) v4i*)(rp + (((4 * t + kc0) ^ kx) << 4));
+        const v4i hi = *(const __attribute__((address_space(3))) v4i*)(rp + (((4 * t + kc0 + 1) ^ kx) << 4));
         sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f8_mfma_operand(lo, hi), qf[t],
                                                                   sacc[kb], 0, 0, 0, 127, 0, 127);
       }
@@ -513,6 +524,8 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdF8Params& p, lds_char* kb0
                                     (fa::lds_char*)v1, (fa::lds_char*)v2);             \
   }
 
+FA_FWD_FP8_KERNEL(fa_fwd_fp8_d32_nomask, 32, 4, false)
+FA_FWD_FP8_KERNEL(fa_fwd_fp8_d32_causal, 32, 4, true)
 FA_FWD_FP8_KERNEL(fa_fwd_fp8_d64_nomask, 64, 4, false)
 FA_FWD_FP8_KERNEL(fa_fwd_fp8_d64_causal, 64, 4, true)
 FA_FWD_FP8_KERNEL(fa_fwd_fp8_d128_nomask, 128, 8, false)
@@ -523,14 +536,15 @@ FA_FWD_FP8_KERNEL(fa_fwd_fp8_d256_causal, 256, 4, true)
 
 namespace fa {
 
-// Waves per workgroup: eight (two per SIMD) at d = 128, four at d = 64
-// (three workgroups per CU) and d = 256 (one).
+// Waves per workgroup: eight (two per SIMD) at d = 128, four at d = 32 (four
+// workgroups per CU), 64 (three) and 256 (one).
 static int fwd_fp8_waves(int d) { return d == 128 ? 8 : 4; }
 
 int fwd_fp8_rows_per_block(int d) { return 32 * fwd_fp8_waves(d); }
 
 const char* fwd_fp8_kernel_name(int d, bool causal) {
   switch (d) {
+    case 32: return causal ? "fa_fwd_fp8_d32_causal" : "fa_fwd_fp8_d32_nomask";
     case 64: return causal ? "fa_fwd_fp8_d64_causal" : "fa_fwd_fp8_d64_nomask";
     case 128: return causal ? "fa_fwd_fp8_d128_causal" : "fa_fwd_fp8_d128_nomask";
     case 256: return causal ? "fa_fwd_fp8_d256_causal" : "fa_fwd_fp8_d256_nomask";
@@ -541,6 +555,7 @@ const char* fwd_fp8_kernel_name(int d, bool causal) {
 hipError_t launch_fwd_fp8(const FwdF8Params& p, int d, bool causal, hipStream_t s) {
   const void* fn = nullptr;
   switch (d) {
+    case 32: fn = causal ? (const void*)fa_fwd_fp8_d32_causal : (const void*)fa_fwd_fp8_d32_nomask; break;
     case 64: fn = causal ? (const void*)fa_fwd_fp8_d64_causal : (const void*)fa_fwd_fp8_d64_nomask; break;
     case 128: fn = causal ? (const void*)fa_fwd_fp8_d128_causal : (const void*)fa_fwd_fp8_d128_nomask; break;
     case 256: fn = causal ? (const void*)fa_fwd_fp8_d256_causal : (const void*)fa_fwd_fp8_d256_nomask; break;

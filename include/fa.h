@@ -44,8 +44,7 @@ enum fa_status {
   FA_ERR_NULL = -1,       /* a required pointer is NULL                      */
   FA_ERR_SHAPE = -2,      /* B, H or N <= 0, Hq % Hkv != 0, causal && Nq > Nk,
                              serving decode Nq outside 1..16                 */
-  FA_ERR_HEAD_DIM = -3,   /* d not in {32, 64, 128, 256} ({64, 128, 256} fp8
-                             forward and fp8 input step)                      */
+  FA_ERR_HEAD_DIM = -3,   /* d not in {32, 64, 128, 256}                     */
   FA_ERR_ALIGN = -4,      /* a tensor pointer is not 16-byte aligned         */
   FA_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required         */
   FA_ERR_SPLITS = -6,     /* num_splits outside 0 .. fa_decode_max_splits()  */
@@ -105,9 +104,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *   k, v      fp8 e4m3 [B][Hkv][Nk][d]
  *   o         bf16 [B][Hq][Nq][d]     output
  *   lse       fp32 [B][Hq][Nq]        output, natural log of the scaled scores
- *   d         64, 128 or 256
+ *   d         32, 64, 128 or 256
  *   scale, q_descale, k_descale, v_descale  finite, > 0
- * Errors as fa_fwd (FA_ERR_HEAD_DIM for d other than 64, 128, 256).
+ * Errors as fa_fwd (FA_ERR_HEAD_DIM for d other than 32, 64, 128, 256).
  */
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
@@ -150,7 +149,7 @@ int fa_fwd_fp8_devscale(const void* q, const void* k, const void* v, void* o, fl
  *   codes     fp8 e4m3 [rows][d]    output
  *   descale   device fp32, 1 value  output (feed to fa_fwd_fp8_devscale)
  *   signs     device int8 [d], negative = -1, otherwise +1; or NULL
- *   d         64, 128 or 256
+ *   d         32, 64, 128 or 256
  *   workspace device scratch of at least fa_fp8_quantize_workspace_size(rows,
  *             d) bytes, 16-byte aligned; its contents on entry do not matter
  * Two kernels on `stream`: the first writes one partial maximum per

@@ -128,7 +128,9 @@ def test_fp8_names_and_quantiser():
     assert fa.fa_fwd_fp8_kernel_name(64, 0) == "fa_fwd_fp8_d64_nomask"
     assert fa.fa_fwd_fp8_kernel_name(256, 1) == "fa_fwd_fp8_d256_causal"
     assert fa.fa_fwd_fp8_kernel_name(256, 0) == "fa_fwd_fp8_d256_nomask"
-    assert fa.fa_fwd_fp8_kernel_name(32, 0) is None
+    assert fa.fa_fwd_fp8_kernel_name(32, 0) == "fa_fwd_fp8_d32_nomask"
+    assert fa.fa_fwd_fp8_kernel_name(32, 1) == "fa_fwd_fp8_d32_causal"
+    assert fa.fa_fwd_fp8_kernel_name(512, 0) is None
     assert fa.fa_fwd_fp8_kernel_name(128, 2) is None
 
 
@@ -338,7 +340,7 @@ def test_serve_rejects(kw, code):
 @cpu_only
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), -1), (dict(o=0), -1), (dict(B=0), -2), (dict(Hq=3), -2), (dict(causal=2), -2),
-    (dict(Nq=65, Nk=64), -2), (dict(d=32), -3), (dict(d=96), -3),
+    (dict(Nq=65, Nk=64), -2), (dict(d=48), -3), (dict(d=96), -3),
     (dict(scale=0.0), -8), (dict(qd=0.0), -8), (dict(kd=math.inf), -8), (dict(vd=-1.0), -8),
     (dict(q=Q + 8), -4), (dict(o=O + 4), -4),
     (dict(o=Q), -9), (dict(lse=K + 16), -9),
@@ -356,10 +358,13 @@ def test_quantize_names_and_workspace():
     assert fa.fa_fp8_quantize_kernel_name(128, 0) == "fa_fp8_absmax_d128"
     assert fa.fa_fp8_quantize_kernel_name(64, 1) == "fa_fp8_quant_d64"
     assert fa.fa_fp8_quantize_kernel_name(256, 0) == "fa_fp8_absmax_d256"
-    assert fa.fa_fp8_quantize_kernel_name(32, 0) is None
+    assert fa.fa_fp8_quantize_kernel_name(32, 0) == "fa_fp8_absmax_d32"
+    assert fa.fa_fp8_quantize_kernel_name(32, 1) == "fa_fp8_quant_d32"
+    assert fa.fa_fp8_quantize_kernel_name(512, 0) is None
     assert fa.fa_fp8_quantize_kernel_name(128, 2) is None
-    # One float per workgroup of the first pass: 64 rows (d = 64), 32
-    # (d = 128) or 16 (d = 256) per workgroup, at most 1024 workgroups.
+    # One float per workgroup of the first pass: 128 rows (d = 32), 64
+    # (d = 64), 32 (d = 128) or 16 (d = 256) per workgroup, at most 1024
+    # workgroups.
     assert fa.fa_fp8_quantize_workspace_size(1, 128) == 4
     assert fa.fa_fp8_quantize_workspace_size(32, 128) == 4
     assert fa.fa_fp8_quantize_workspace_size(33, 128) == 8
@@ -370,6 +375,8 @@ def test_quantize_names_and_workspace():
     assert fa.fa_fp8_quantize_workspace_size(16, 256) == 4
     assert fa.fa_fp8_quantize_workspace_size(17, 256) == 8
     assert fa.fa_fp8_quantize_workspace_size(16, 512) == 0
+    assert fa.fa_fp8_quantize_workspace_size(128, 32) == 4
+    assert fa.fa_fp8_quantize_workspace_size(129, 32) == 8
 
 
 S8 = 0x700000   # placeholder address of the signs vector
@@ -379,7 +386,7 @@ DS = 0x800000   # placeholder address of the descale output
 @cpu_only
 @pytest.mark.parametrize("kw,code", [
     (dict(x=0), -1), (dict(codes=0), -1), (dict(ds=0), -1),
-    (dict(rows=0), -2), (dict(rows=-5), -2), (dict(d=32), -3), (dict(d=512), -3),
+    (dict(rows=0), -2), (dict(rows=-5), -2), (dict(d=48), -3), (dict(d=512), -3),
     (dict(x=Q + 8), -4), (dict(codes=O + 4), -4), (dict(ds=DS + 2), -4),
     (dict(ws=0), -5), (dict(wsb=4), -5), (dict(ws=W + 4), -4),
     (dict(codes=Q + 64), -9), (dict(ds=Q + 16), -9), (dict(ws=O), -9),
@@ -394,7 +401,7 @@ def test_quantize_rejects(kw, code):
 
 @cpu_only
 @pytest.mark.parametrize("kw,code", [
-    (dict(qd=0), -1), (dict(vd=0), -1), (dict(q=0), -1), (dict(d=32), -3),
+    (dict(qd=0), -1), (dict(vd=0), -1), (dict(q=0), -1), (dict(d=48), -3),
     (dict(scale=0.0), -8), (dict(kd=DS + 2), -4), (dict(qd=O + 64), -9), (dict(vd=L), -9),
     (dict(B=0), -2),
 ])

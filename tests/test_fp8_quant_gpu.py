@@ -71,6 +71,9 @@ CASES = [  # (rows, d, rotated, outliers)
     # rotation); 5 rows: part of one wave's row group
     (5, 256, True, False), (1000, 256, True, True), (3001, 256, False, False),
     (20000, 256, True, False),
+    # d = 32: two lanes per row, one butterfly between lanes
+    (3, 32, True, False), (1000, 32, True, True), (4099, 32, False, False),
+    (50001, 32, True, False),
 ]
 
 
@@ -153,7 +156,8 @@ def _oracle_pipeline(qb, kb, vb, signs, causal, scale):
 
 E2E = [(1, 4, 2, 200, 200, 128, True), (1, 2, 2, 130, 300, 64, False),
        (2, 4, 4, 257, 257, 128, False), (1, 8, 2, 64, 1000, 128, True),
-       (1, 2, 1, 200, 200, 256, True), (1, 4, 2, 130, 300, 256, False)]
+       (1, 2, 1, 200, 200, 256, True), (1, 4, 2, 130, 300, 256, False),
+       (1, 2, 1, 200, 200, 32, True), (1, 4, 2, 130, 300, 32, False)]
 
 
 @pytest.mark.parametrize("shape", E2E, ids=[

@@ -79,6 +79,15 @@ ODD = [
     (1, 2, 1, 129, 190, 256, False),
     (2, 2, 2, 130, 130, 256, True),
     (1, 8, 4, 300, 1100, 256, False),
+    # d = 32: one k-step with the upper lane half zero, 32-byte LDS rows;
+    # tails, GQA, Nq < Nk, one and two key tiles, head-major order
+    (1, 2, 1, 200, 200, 32, False),
+    (1, 2, 1, 200, 200, 32, True),
+    (1, 4, 2, 77, 300, 32, True),
+    (2, 2, 2, 130, 130, 32, True),
+    (1, 8, 4, 300, 1100, 32, False),
+    (1, 2, 1, 64, 64, 32, True),
+    (1, 3, 1, 40, 100, 32, False),
 ]
 
 
@@ -133,8 +142,12 @@ def test_fp8_sweep_d256_sampled():
     _workload("sweep_d256", [(0, 0), (1, 13)], 256)
 
 
+def test_fp8_sweep_d32_sampled():
+    _workload("sweep_d32", [(0, 0), (1, 9)], 256)
+
+
 @pytest.mark.parametrize("slope", [0.2, 1.0, -1.0])
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 def test_fp8_drifting_scores(slope, d):
     """Rising scores exceed the reference maximum by far more than 2^8 in
     tile after tile, so the tile's probabilities are redone against a new
